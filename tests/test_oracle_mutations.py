@@ -1,0 +1,111 @@
+"""The pins catch plausible mistakes: each case plants one into the oracle (CPU only,
+through monkeypatch) and expects at least one of the pin tests to fail."""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.e4m3 as e4m3
+import oracle.linear as linear
+import oracle.quant as quant
+from tests import test_oracle_e4m3 as te
+from tests import test_oracle_linear as tl
+from tests import test_oracle_quant as tq
+from tests import test_oracle_silu as ts
+
+
+def _fails(fn):
+    try:
+        fn()
+    except (AssertionError, ValueError):
+        return True
+    return False
+
+
+def _encode_ties_away(v):
+    v = np.asarray(v, dtype=np.float32)
+    a = np.minimum(np.abs(v.astype(np.float64)), 448.0)
+    mags = e4m3._MAGS
+    hi = np.minimum(np.searchsorted(mags, a), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    take_hi = (mags[hi] - a) <= (a - mags[lo])
+    return (np.where(take_hi, hi, lo).astype(np.uint8) | (np.signbit(v).astype(np.uint8) << 7))
+
+
+def _encode_no_sign(v):
+    return e4m3.encode_rne_sat(np.abs(np.asarray(v, dtype=np.float32)))
+
+
+def _quant_groups_reciprocal(x, axes):
+    amax = np.max(np.abs(x), axis=axes, keepdims=True)
+    s = (amax * np.float32(1.0 / 448.0)).astype(np.float32)
+    zero = s == 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = (x / np.where(zero, np.float32(1), s)).astype(np.float32)
+    q = e4m3.encode_rne_sat(np.clip(v, -448, 448))
+    q = np.where(np.broadcast_to(zero, q.shape), np.uint8(0), q).astype(np.uint8)
+    return q, np.squeeze(s, axis=axes).astype(np.float32)
+
+
+def _quant_act_strided_groups(x_bits):
+    M, K = x_bits.shape
+    x = quant.bf16_bits_to_f32(x_bits).reshape(M, 128, K // 128)
+    q, s = quant._quant_groups(x, axes=(1,))
+    return q.reshape(M, K), s.reshape(M, K // 128)
+
+
+def _dequant_weight_transposed(qw, ws):
+    N, K = qw.shape
+    w = e4m3.decode(qw).reshape(N // 128, 128, K // 128, 128)
+    wsT = np.asarray(ws, np.float32).T.reshape(ws.shape)      # scrambled grid
+    return (w * wsT.astype(np.float64)[:, None, :, None]).reshape(N, K)
+
+
+def _dequant_act_no_scale(q, s):
+    return e4m3.decode(q).astype(np.float64)
+
+
+def _silu_wrong_sign(gu_bits):
+    gu = quant.bf16_bits_to_f32(gu_bits).astype(np.float64)
+    h = gu.shape[1] // 2
+    g, u = gu[:, :h], gu[:, h:]
+    with np.errstate(over="ignore"):
+        return quant.f64_to_bf16_bits(g / (1.0 + np.exp(g)) * u)
+
+
+def _silu_via_f32(gu_bits):
+    gu = quant.bf16_bits_to_f32(gu_bits)
+    h = gu.shape[1] // 2
+    g, u = gu[:, :h], gu[:, h:]
+    with np.errstate(over="ignore"):
+        r = (g / (np.float32(1) + np.exp(-g)) * u).astype(np.float32)
+    return quant.f64_to_bf16_bits(r.astype(np.float64))   # double rounding
+
+
+MUTATIONS = {
+    "ties_away_from_zero": ([(e4m3, "encode_rne_sat", _encode_ties_away), (quant, "encode_rne_sat", _encode_ties_away),
+                             (oracle, "encode_rne_sat", _encode_ties_away)],
+                            [te.test_midpoints_round_to_even_and_neighbours_to_nearer]),
+    "sign_dropped": ([(quant, "encode_rne_sat", _encode_no_sign)],
+                     [tq.test_negation_flips_sign_bits_only]),
+    "scale_by_reciprocal": ([(quant, "_quant_groups", _quant_groups_reciprocal)],
+                            [tq.test_scale_is_correctly_rounded_amax_over_448]),
+    "strided_groups": ([(quant, "quant_act", _quant_act_strided_groups), (oracle, "quant_act", _quant_act_strided_groups)],
+                       [tq.test_group_structure_spike]),
+    "weight_grid_transposed": ([(linear, "dequant_weight", _dequant_weight_transposed)],
+                               [tl.test_matches_exact_rational_triple_loop]),
+    "activation_scale_dropped": ([(linear, "dequant_act", _dequant_act_no_scale)],
+                                 [tl.test_matches_exact_rational_triple_loop]),
+    "silu_sign": ([(quant, "silu_mul_bf16", _silu_wrong_sign), (oracle, "silu_mul_bf16", _silu_wrong_sign)],
+                  [ts.test_silu_special_values]),
+    "silu_double_rounding": ([(quant, "silu_mul_bf16", _silu_via_f32), (oracle, "silu_mul_bf16", _silu_via_f32)],
+                             [ts.test_silu_mul_matches_high_precision_reference, ts.test_silu_mul_near_rounding_midpoints]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    patches, pins = MUTATIONS[name]
+    for mod, attr, fn in patches:
+        monkeypatch.setattr(mod, attr, fn)
+    assert any(_fails(p) for p in pins), f"planted mistake {name} went unnoticed"
