@@ -1,0 +1,272 @@
+"""Benchmark of the W8A8 FP8 block-scaled linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_qkv]
+                    [--no-cpu-baseline] [--no-others] [--traffic-file PATH]
+
+A step is one pass of the hot path over one batch: dynamic per-token group-128
+activation quantization of the BF16 input, then the block-scaled FP8 GEMM
+(weights were block-quantized once, untimed, as the offline step they are).
+The headline workload is the decode fused-QKV projection (M=1, K=7168, N=9216),
+whose metric is achieved GB/s: its weight stream is 99.9% of its bytes.  Inputs
+are resident in HBM before timing; weight copies are rotated so that the weights
+touched between two uses of one copy exceed twice the 256 MB Infinity Cache.
+
+Timing: W untimed warm-up steps, then K steps bracketed by device synchronization.
+Each launch of the dominant kernel (the GEMM) is bracketed by HIP events on the
+stream it runs on, giving its average duration for the roofline.
+
+Printed: ONE JSON line.  Besides the contract fields it carries the other
+workloads' numbers ("workloads"), measured the same way.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+MALL_BYTES = 256 << 20         # Infinity Cache
+METRIC = "FP8 block-GEMM TFLOP/s (prefill) and GB/s (decode M=1..8), % of roofline"
+KERNEL_SOURCES = ["gemm_decode.hip", "gemm_prefill.hip", "quant.hip", "device_common.h", "api.hip"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "fp8_block_scaled_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode_qkv")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    p.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    return p.parse_args()
+
+
+def dev_bf16(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class Case:
+    """Device-resident inputs and preallocated outputs of one linear workload."""
+
+    def __init__(self, wl, x_bits=None, gu_bits=None):
+        import torch
+        import fp8_block_scaled_amd as fb
+        import synth
+        self.wl = wl
+        M, K, N = wl.M, wl.K, wl.N
+        wbytes = N * K
+        self.copies = max(1, min(16, -(-2 * MALL_BYTES // wbytes)))
+        w = synth.make_weight(wl)
+        wd = dev_bf16(w)
+        qw, ws = fb.quant_weight(wd)
+        del wd
+        self.qw = [qw] + [qw.clone() for _ in range(self.copies - 1)]
+        self.ws = [ws] + [ws.clone() for _ in range(self.copies - 1)]
+        if gu_bits is not None:       # down projection: its input is SiLU(gate)*up of a gate/up tensor
+            self.gu = dev_bf16(gu_bits)
+            self.x = None
+        else:
+            self.x = dev_bf16(x_bits if x_bits is not None else synth.make_activation(wl))
+            self.gu = None
+        self.q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        self.s = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+        self.y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        need = fb.workspace_size(M, N, K)
+        self.workspace = fb.get_workspace("cuda", need) if need else None
+        torch.cuda.synchronize()
+
+    def quant(self):
+        import fp8_block_scaled_amd as fb
+        if self.gu is not None:
+            fb.silu_mul_quant(self.gu, self.q, self.s)
+        else:
+            fb.quant_act(self.x, self.q, self.s)
+
+    def gemm(self, i):
+        import fp8_block_scaled_amd as fb
+        c = i % self.copies
+        fb.block_linear(self.q, self.s, self.qw[c], self.ws[c], out=self.y, workspace=self.workspace)
+
+
+def time_case(case, steps, warmup):
+    """Run warmup + timed steps; return (ms per step, avg GEMM us, avg quant us)."""
+    import torch
+    for i in range(warmup):
+        case.quant()
+        case.gemm(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(steps):
+        e0, e1, e2 = ev[i]
+        e0.record()
+        case.quant()
+        e1.record()
+        case.gemm(i)
+        e2.record()
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    quant_us = sum(a.elapsed_time(b) for a, b, _ in ev) * 1e3 / steps
+    gemm_us = sum(b.elapsed_time(c) for _, b, c in ev) * 1e3 / steps
+    return total_ms / steps, gemm_us, quant_us
+
+
+def roofline_for(wl, gemm_us, traffic):
+    if wl.M <= 16:
+        achieved = wl.gemm_bytes() / (gemm_us * 1e-6) / 1e9
+        r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = wl.gemm_flops() / (gemm_us * 1e-6) / 1e12
+        r = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(achieved / FP8_PEAK_TFLOPS, 4)}
+    r["traffic"] = traffic
+    return r
+
+
+def load_traffic(path, workload):
+    """HBM bytes per GEMM dispatch from committed rocprofv3 counter runs, or None when
+    absent or taken on different kernel sources."""
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    ent = t.get("workloads", {}).get(workload)
+    return ent.get("bytes_per_dispatch") if ent else None
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle, as it stands, on the same workload: quantize the activation row(s)
+    and dequantize-and-matmul in float64, repeated for about budget_s seconds."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    x = synth.make_activation(wl)
+    w = synth.make_weight(wl)
+    qw, ws = oracle.quant_weight(w)            # offline step, untimed as on the GPU
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        q, s = oracle.quant_act(x)
+        oracle.linear_ref(q, s, qw, ws)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    per_step = el / reps
+    bytes_step = wl.quant_bytes() + wl.gemm_bytes()
+    return {"value": round(bytes_step / per_step / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": (f"{reps} full steps of {wl.name} (M={wl.M}, K={wl.K}, N={wl.N}): numpy quantizer "
+                       f"(1 thread) + float64 dequantize-and-matmul (BLAS, {blas_threads} threads), "
+                       f"{el:.1f} s, {per_step * 1e3:.1f} ms/step")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+    import synth
+    from synth import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    wl = WORKLOADS[args.workload]
+    print(f"[bench] {wl.name}: setup", file=sys.stderr, flush=True)
+    case = Case(wl)
+    ms, gemm_us, quant_us = time_case(case, args.steps, args.warmup)
+    step_bytes = wl.quant_bytes() + wl.gemm_bytes()
+    value = step_bytes / (ms * 1e-3) / 1e9
+    traffic = load_traffic(args.traffic_file, wl.name)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 in/out)",
+        "data": "synthetic (seeded; Philox per-row streams)",
+        "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N,
+                   "step": "quant_act + block_linear", "weight_copies_rotated": case.copies,
+                   "step_bytes": step_bytes},
+        "roofline": roofline_for(wl, gemm_us, traffic),
+        "kernels_us": {"block_linear": round(gemm_us, 2), "quant_act": round(quant_us, 2)},
+    }
+    del case
+    torch.cuda.empty_cache()
+
+    if not args.no_others:
+        others = {}
+        order = ["tiny", "spec_mlp_gu", "spec_mlp_down", "prefill_oproj", "fusion_fc"]
+        for name in order:
+            if name == wl.name:
+                continue
+            w2 = WORKLOADS[name]
+            print(f"[bench] {name}: setup", file=sys.stderr, flush=True)
+            if name == "spec_mlp_down":
+                gu = synth.bf16_normal(8, 16384, 1.7, w2.seed, synth.TID_GU)
+                c2 = Case(w2, gu_bits=gu)
+            else:
+                c2 = Case(w2)
+            steps = max(5, min(args.steps, 50 if w2.M > 16 else args.steps))
+            ms2, g2, q2 = time_case(c2, steps, max(2, min(args.warmup, 5)))
+            rl = roofline_for(w2, g2, load_traffic(args.traffic_file, name))
+            others[name] = {"M": w2.M, "K": w2.K, "N": w2.N, "ms_per_step": round(ms2, 5),
+                            "block_linear_us": round(g2, 2), "quant_us": round(q2, 2),
+                            "gemm_roofline": rl, "weight_copies_rotated": c2.copies}
+            del c2
+            torch.cuda.empty_cache()
+        out["workloads"] = others
+
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,142 @@
+"""MI355X (gfx950) W8A8 FP8 block-scaled linear.
+
+Thin torch-facing binding over libfp8bs.so (include/fp8bs.h).  Torch supplies
+device memory and the current stream; every step of the computation runs in the
+library's HIP kernels.  The wrappers only check dtypes/devices/contiguity, allocate
+outputs and pass raw pointers.
+
+    q, s = quant_act(x)                       # x: bf16 [M, K] on a gfx950 device
+    qw, ws = quant_weight(w)                  # w: bf16 [N, K]
+    y = block_linear(q, s, qw, ws)            # y: bf16 [M, N]
+    q2, s2 = silu_mul_quant(gu)               # gu: bf16 [M, 2I] -> codes of BF16(silu(g)*u)
+
+Tensor dtypes: BF16 tensors are torch.bfloat16; E4M3 codes are torch.uint8 (view
+them as torch.float8_e4m3fn if wanted); scales are torch.float32.
+"""
+
+import torch
+
+from ._lib import Fp8bsError, check, lib  # noqa: F401
+
+__all__ = [
+    "quant_act",
+    "quant_weight",
+    "silu_mul_quant",
+    "block_linear",
+    "workspace_size",
+    "get_workspace",
+    "Fp8bsError",
+]
+
+_workspaces = {}
+
+
+def _stream(device):
+    return ctypes_stream(torch.cuda.current_stream(device))
+
+
+def ctypes_stream(stream):
+    return stream.cuda_stream
+
+
+def _check_tensor(t, name, dtypes, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (there is no CPU path)")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16) if hasattr(torch, "uint16") else (torch.bfloat16, torch.int16)
+_CODES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def quant_act(x, q=None, s=None):
+    """Per-token group-128 quantization of BF16 x [M, K] -> (q uint8 [M, K], s f32 [M, K/128])."""
+    _check_tensor(x, "x", _BF16, 2)
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
+    s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if s is None else s
+    with torch.cuda.device(x.device):
+        check("fp8_quant_act", lib().fp8_quant_act(x.data_ptr(), q.data_ptr(), s.data_ptr(), M, K, _stream(x.device)))
+    return q, s
+
+
+def quant_weight(w):
+    """128x128 block quantization of BF16 w [N, K] -> (qw uint8 [N, K], ws f32 [N/128, K/128])."""
+    _check_tensor(w, "w", _BF16, 2)
+    N, K = w.shape
+    qw = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+    with torch.cuda.device(w.device):
+        check("fp8_quant_weight",
+              lib().fp8_quant_weight(w.data_ptr(), qw.data_ptr(), ws.data_ptr(), N, K, _stream(w.device)))
+    return qw, ws
+
+
+def silu_mul_quant(gu, q=None, s=None):
+    """Codes and scales of BF16(silu(gate) * up) for gu = [gate | up], BF16 [M, 2I]."""
+    _check_tensor(gu, "gu", _BF16, 2)
+    M, two_i = gu.shape
+    if two_i % 2:
+        raise ValueError("gate/up width must be even")
+    I = two_i // 2
+    q = torch.empty((M, I), dtype=torch.uint8, device=gu.device) if q is None else q
+    s = torch.empty((M, I // 128), dtype=torch.float32, device=gu.device) if s is None else s
+    with torch.cuda.device(gu.device):
+        check("fp8_silu_mul_quant",
+              lib().fp8_silu_mul_quant(gu.data_ptr(), q.data_ptr(), s.data_ptr(), M, I, _stream(gu.device)))
+    return q, s
+
+
+def workspace_size(M, N, K):
+    return int(lib().fp8_block_linear_workspace_size(M, N, K))
+
+
+def get_workspace(device, nbytes):
+    """A zero-filled workspace of at least ``nbytes`` for ``device``, cached per device.
+
+    The library leaves it zero-filled after every completed call, so it is reused
+    as is.  Calls on one device through this cache share it: they must be ordered
+    (one stream), as the library requires for a shared workspace.
+    """
+    device = torch.device(device)
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        size = max(nbytes, 1 << 20)
+        size = (size + 255) // 256 * 256
+        ws = torch.zeros(size, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def block_linear(q, s, qw, ws, out=None, workspace=None):
+    """y [M, N] bf16 = (q * s) @ (qw * ws)^T with FP32 accumulation per 128-wide K block."""
+    _check_tensor(q, "q", _CODES, 2)
+    _check_tensor(s, "s", (torch.float32,), 2)
+    _check_tensor(qw, "qw", _CODES, 2)
+    _check_tensor(ws, "ws", (torch.float32,), 2)
+    M, K = q.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K:
+        raise ValueError("q and qw disagree on K")
+    if s.shape != (M, K // 128) or ws.shape != (N // 128, K // 128):
+        raise ValueError("scale shapes do not match the operands")
+    dev = q.device
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    if workspace is None:
+        need = workspace_size(M, N, K) if K > 0 else 0
+        workspace = get_workspace(dev, need) if need else None
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with torch.cuda.device(dev):
+        check("fp8_block_linear",
+              lib().fp8_block_linear(q.data_ptr(), s.data_ptr(), qw.data_ptr(), ws.data_ptr(), y.data_ptr(),
+                                     M, N, K, wptr, wbytes, _stream(dev)))
+    return y

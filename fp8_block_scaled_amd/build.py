@@ -1,0 +1,73 @@
+"""Build libfp8bs.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
+
+    python -m fp8_block_scaled_amd.build          # or fp8_block_scaled_amd.build.build()
+
+Objects go to fp8_block_scaled_amd/_build/, the library to
+fp8_block_scaled_amd/libfp8bs.so.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libfp8bs.so")
+SOURCES = ["api.hip", "quant.hip", "gemm_decode.hip", "gemm_prefill.hip"]
+
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+CFLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    # No packed FP32 instructions in device code.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # IEEE float32 division and FP32 denormals: the quantizer is bit-exact only with both.
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-fno-gpu-flush-denormals-to-zero",
+    "-ffp-contract=fast",
+    "-Wall",
+    "-Wno-unused-function",
+    f"-I{os.path.join(ROOT, 'include')}",
+    f"-I{CSRC}",
+]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in p.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"command failed ({p.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out, flush=True)
+
+
+def build(verbose=False, jobs=None):
+    """Compile every HIP source for gfx950 and link libfp8bs.so.  Always rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+
+    def compile_one(src):
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        _run([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        return obj
+
+    with ThreadPoolExecutor(jobs or min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,128 @@
+// C ABI of libfp8bs.so (declared in include/fp8bs.h).
+//
+// Every entry point validates its arguments on the host before touching the HIP
+// runtime, so argument errors are reported synchronously and identically with or
+// without a GPU.  Then it checks (once per device, cached) that the current device
+// is gfx950, and enqueues the kernels on the caller's stream.
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "fp8bs.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = not yet queried, > 0 = gfx950 with that many CUs, < 0 = not gfx950.
+std::atomic<int> g_device_cus[kMaxDevices];
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Sizes must be non-negative and every element/byte count must fit int64.
+bool mul_ok(int64_t a, int64_t b) { return a == 0 || b <= INT64_MAX / a; }
+
+int check_device(int* cus_out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FP8BS_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FP8BS_ERR_DEVICE;
+    int v = g_device_cus[dev].load(std::memory_order_acquire);
+    if (v == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8BS_ERR_HIP;
+        const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        v = ok ? (prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1) : -1;
+        g_device_cus[dev].store(v, std::memory_order_release);
+    }
+    if (v < 0) return FP8BS_ERR_DEVICE;
+    if (cus_out) *cus_out = v;
+    return FP8BS_OK;
+}
+
+int quant_shape_check(const void* in, const void* q, const float* s, int64_t M, int64_t K) {
+    if (M < 0 || K < 0 || K % 128 != 0 || !mul_ok(M, K) || !mul_ok(M * K, 2)) return FP8BS_ERR_SHAPE;
+    if (M == 0 || K == 0) return 1;   // nothing to do
+    if (!in || !q || !s) return FP8BS_ERR_NULL;
+    if (!aligned(in, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8BS_ERR_ALIGN;
+    return FP8BS_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fp8bs_abi_version(void) { return FP8BS_ABI_VERSION; }
+
+const char* fp8bs_status_string(int status) {
+    switch (status) {
+        case FP8BS_OK: return "ok";
+        case FP8BS_ERR_NULL: return "a required pointer is NULL";
+        case FP8BS_ERR_SHAPE: return "invalid shape (negative size, K or N not a multiple of 128, or overflow)";
+        case FP8BS_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte, scales 4-byte alignment)";
+        case FP8BS_ERR_DEVICE: return "the current HIP device is not gfx950 (MI355X)";
+        case FP8BS_ERR_HIP: return "HIP runtime call or kernel launch failed";
+        case FP8BS_ERR_WORKSPACE: return "workspace must be 256-byte aligned";
+        default: return "unknown fp8bs status";
+    }
+}
+
+int fp8_quant_act(const void* x_bf16, void* q_e4m3, float* s_f32, int64_t M, int64_t K, hipStream_t stream) {
+    int rc = quant_shape_check(x_bf16, q_e4m3, s_f32, M, K);
+    if (rc != FP8BS_OK) return rc > 0 ? FP8BS_OK : rc;
+    if ((rc = check_device(nullptr)) != FP8BS_OK) return rc;
+    return hip_status(fp8bs::launch_quant_act(x_bf16, q_e4m3, s_f32, M, K, stream));
+}
+
+int fp8_quant_weight(const void* w_bf16, void* qw_e4m3, float* ws_f32, int64_t N, int64_t K, hipStream_t stream) {
+    if (N < 0 || N % 128 != 0) return FP8BS_ERR_SHAPE;
+    int rc = quant_shape_check(w_bf16, qw_e4m3, ws_f32, N, K);
+    if (rc != FP8BS_OK) return rc > 0 ? FP8BS_OK : rc;
+    if ((rc = check_device(nullptr)) != FP8BS_OK) return rc;
+    return hip_status(fp8bs::launch_quant_weight(w_bf16, qw_e4m3, ws_f32, N, K, stream));
+}
+
+int fp8_silu_mul_quant(const void* gu_bf16, void* q_e4m3, float* s_f32, int64_t M, int64_t I, hipStream_t stream) {
+    if (I < 0 || !mul_ok(I, 2)) return FP8BS_ERR_SHAPE;
+    int rc = quant_shape_check(gu_bf16, q_e4m3, s_f32, M, I);
+    if (rc == FP8BS_OK && !mul_ok(M, 2 * I)) rc = FP8BS_ERR_SHAPE;
+    if (rc != FP8BS_OK) return rc > 0 ? FP8BS_OK : rc;
+    if ((rc = check_device(nullptr)) != FP8BS_OK) return rc;
+    return hip_status(fp8bs::launch_silu_mul_quant(gu_bf16, q_e4m3, s_f32, M, I, stream));
+}
+
+size_t fp8_block_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K <= 0 || N % 128 || K % 128 || !mul_ok(N, K) || !mul_ok(M, K) || !mul_ok(M, N))
+        return 0;
+    if (M == 0 || N == 0 || M > fp8bs::kDecodeMaxM) return 0;
+    int cus = 256;
+    if (check_device(&cus) != FP8BS_OK) cus = 256;
+    return fp8bs::decode_workspace_bytes(fp8bs::plan_decode(M, N, K, cus, true));
+}
+
+int fp8_block_linear(const void* q_e4m3, const float* s_f32, const void* w_e4m3, const float* ws_f32,
+                     void* y_bf16, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+    if (M < 0 || N < 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
+    if (!mul_ok(N, K) || !mul_ok(M, K) || !mul_ok(M, N) || !mul_ok(M * N, 2)) return FP8BS_ERR_SHAPE;
+    if (M == 0 || N == 0) return FP8BS_OK;
+    if (!q_e4m3 || !s_f32 || !w_e4m3 || !ws_f32 || !y_bf16) return FP8BS_ERR_NULL;
+    if (!aligned(q_e4m3, 16) || !aligned(w_e4m3, 16) || !aligned(y_bf16, 16) || !aligned(s_f32, 4) ||
+        !aligned(ws_f32, 4))
+        return FP8BS_ERR_ALIGN;
+    if (workspace && !aligned(workspace, 256)) return FP8BS_ERR_WORKSPACE;
+    int cus = 0;
+    int rc = check_device(&cus);
+    if (rc != FP8BS_OK) return rc;
+    if (M <= fp8bs::kDecodeMaxM) {
+        fp8bs::DecodePlan plan = fp8bs::plan_decode(M, N, K, cus, true);
+        if (plan.split && (!workspace || workspace_bytes < fp8bs::decode_workspace_bytes(plan)))
+            plan = fp8bs::plan_decode(M, N, K, cus, false);
+        return hip_status(
+            fp8bs::launch_gemm_decode(plan, q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, workspace, stream));
+    }
+    return hip_status(fp8bs::launch_gemm_prefill(q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, cus, stream));
+}
+
+}  // extern "C"

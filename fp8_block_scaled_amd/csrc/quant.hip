@@ -1,0 +1,183 @@
+// Quantization kernels for gfx950:
+//   quant_act_kernel       dynamic per-token, group-128 activation quantization
+//   silu_mul_quant_kernel  h = BF16(silu(gate) * up) in FP64, then the same quantization
+//   quant_weight_kernel    128x128 block weight quantization (offline step)
+//
+// Scheme: "Nanbeige4.3-33B FP8" model card, introduction and "Recipe and
+// calibration" (E4M3 weights in 128x128 blocks, minmax scales; dynamic per-token
+// group-128 activation scales).  Scale = fl32(amax / 448); code = E4M3 of
+// fl32(x / scale), nearest even, saturated at 448; an all-zero group has scale +0
+// and codes 0x00.
+//
+// Activation layout: K is a multiple of 128, so the groups of [M, K] row-major
+// data are consecutive 256-byte runs and group g's scale sits at s[g] of the
+// row-major [M, K/128] scale tensor: the activation quantizer is a flat loop over
+// groups.  One group is handled by one 16-lane DPP row: each lane loads 8 BF16
+// (16 bytes), the group amax is a 4-step DPP max, and each lane stores 8 codes.
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8bs {
+
+constexpr int kQuantThreads = 256;           // 16 groups per block pass
+constexpr int kQuantUnroll = 4;              // groups per 16-lane row per block
+
+struct Bf16x8 { uint4 v; };
+
+__device__ __forceinline__ void unpack8(const uint4& v, float (&x)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+
+// Codes of 8 values of one group (scale s, already reduced over the group).
+__device__ __forceinline__ uint2 quant8(const float (&x)[8], float s) {
+    uint32_t c[8];
+    if (s == 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = 0;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = quant_one(x[i], s);
+    }
+    uint2 out;
+    out.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    out.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    return out;
+}
+
+__device__ __forceinline__ float absmax8(const float (&x)[8]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+    return m;
+}
+
+// Groups [blockIdx.x * 16 * U, +16 * U): pass u handles groups base + 16 u + row.
+__global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ s, int64_t n_groups) {
+    const int row = threadIdx.x >> 4;
+    const int sub = threadIdx.x & 15;
+    const int64_t base = (int64_t)blockIdx.x * (16 * kQuantUnroll);
+    uint4 raw[kQuantUnroll];
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+        const int64_t g = base + 16 * u + row;
+        if (g < n_groups)
+            raw[u] = reinterpret_cast<const uint4*>(x + g * kGroup)[sub];
+    }
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+        const int64_t g = base + 16 * u + row;
+        if (g >= n_groups) continue;             // uniform over the 16-lane row
+        float v[8];
+        unpack8(raw[u], v);
+        const float amax = row16_max(absmax8(v));
+        const float sc = amax / kE4M3Max;
+        reinterpret_cast<uint2*>(q + g * kGroup)[sub] = quant8(v, sc);
+        if (sub == 0) s[g] = sc;
+    }
+}
+
+// gu [M, 2I]: gate = columns [0, I), up = [I, 2I).  Group g of h: row g / (I/128),
+// columns 128 (g % (I/128)) + [0, 128).
+__global__ __launch_bounds__(kQuantThreads) void silu_mul_quant_kernel(
+    const uint16_t* __restrict__ gu, uint8_t* __restrict__ q, float* __restrict__ s,
+    int64_t n_groups, int64_t groups_per_row, int64_t I) {
+    const int row = threadIdx.x >> 4;
+    const int sub = threadIdx.x & 15;
+    const int64_t base = (int64_t)blockIdx.x * (16 * kQuantUnroll);
+    uint4 graw[kQuantUnroll], uraw[kQuantUnroll];
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+        const int64_t g = base + 16 * u + row;
+        if (g < n_groups) {
+            const int64_t m = g / groups_per_row, j = g - m * groups_per_row;
+            const uint16_t* p = gu + m * 2 * I + j * kGroup;
+            graw[u] = reinterpret_cast<const uint4*>(p)[sub];
+            uraw[u] = reinterpret_cast<const uint4*>(p + I)[sub];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+        const int64_t g = base + 16 * u + row;
+        if (g >= n_groups) continue;
+        float gv[8], uv[8], h[8];
+        unpack8(graw[u], gv);
+        unpack8(uraw[u], uv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double gd = (double)gv[i];
+            const double silu = gd / (1.0 + exp(-gd));
+            h[i] = bf16_to_f32(f64_to_bf16_rne(silu * (double)uv[i]));
+        }
+        const float amax = row16_max(absmax8(h));
+        const float sc = amax / kE4M3Max;
+        reinterpret_cast<uint2*>(q + g * kGroup)[sub] = quant8(h, sc);
+        if (sub == 0) s[g] = sc;
+    }
+}
+
+// One 256-thread block per 128x128 weight block.  Thread t covers row t / 2 of the
+// block, columns 64 (t % 2) + [0, 64).
+__global__ __launch_bounds__(256) void quant_weight_kernel(
+    const uint16_t* __restrict__ w, uint8_t* __restrict__ qw, float* __restrict__ ws,
+    int64_t N, int64_t K) {
+    __shared__ float wave_amax[4];
+    const int64_t kblocks = K / kGroup;
+    const int64_t bi = blockIdx.x / kblocks, bj = blockIdx.x % kblocks;
+    const int t = threadIdx.x;
+    const int64_t r = bi * kGroup + (t >> 1);
+    const int64_t c = bj * kGroup + (t & 1) * 64;
+    const uint4* src = reinterpret_cast<const uint4*>(w + r * K + c);
+    float v[8][8];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        unpack8(src[i], v[i]);
+        m = fmaxf(m, absmax8(v[i]));
+    }
+    m = wave_max(m);
+    if ((t & 63) == 0) wave_amax[t >> 6] = m;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(wave_amax[0], wave_amax[1]), fmaxf(wave_amax[2], wave_amax[3]));
+    const float sc = amax / kE4M3Max;
+    uint2* dst = reinterpret_cast<uint2*>(qw + r * K + c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = quant8(v[i], sc);
+    if (t == 0) ws[blockIdx.x] = sc;
+}
+
+hipError_t launch_quant_act(const void* x, void* q, float* s, int64_t M, int64_t K, hipStream_t st) {
+    const int64_t n_groups = M * (K / kGroup);
+    if (n_groups == 0) return hipSuccess;
+    const int64_t per_block = 16 * kQuantUnroll;
+    const int64_t blocks = (n_groups + per_block - 1) / per_block;
+    hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0, st,
+                       (const uint16_t*)x, (uint8_t*)q, s, n_groups);
+    return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_quant(const void* gu, void* q, float* s, int64_t M, int64_t I, hipStream_t st) {
+    const int64_t gpr = I / kGroup;
+    const int64_t n_groups = M * gpr;
+    if (n_groups == 0) return hipSuccess;
+    const int64_t per_block = 16 * kQuantUnroll;
+    const int64_t blocks = (n_groups + per_block - 1) / per_block;
+    hipLaunchKernelGGL(silu_mul_quant_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0, st,
+                       (const uint16_t*)gu, (uint8_t*)q, s, n_groups, gpr, I);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weight(const void* w, void* qw, float* ws, int64_t N, int64_t K, hipStream_t st) {
+    const int64_t nblocks = (N / kGroup) * (K / kGroup);
+    if (nblocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_weight_kernel, dim3((unsigned)nblocks), dim3(256), 0, st,
+                       (const uint16_t*)w, (uint8_t*)qw, ws, N, K);
+    return hipGetLastError();
+}
+
+}  // namespace fp8bs

@@ -1,0 +1,126 @@
+/*
+ * fp8bs.h -- C ABI of libfp8bs.so, the MI355X (gfx950) W8A8 FP8 block-scaled linear.
+ *
+ * The operation is the linear layer of the "Nanbeige4.3-33B FP8" model card
+ * (ProCreations; introduction and section "Recipe and calibration"): weights in
+ * OCP E4M3 with one scale per 128x128 block ("standard minmax"), activations
+ * quantized dynamically per token in groups of 128, the GEMM accumulated in FP32
+ * and written as BF16 (the model is served with --dtype bfloat16, section
+ * "Serving").  The card fixes no API; these calls are this library's own.
+ *
+ * Conventions shared by every call:
+ *   - All tensors are dense, row-major and live in device memory of the current
+ *     HIP device.  The caller owns every buffer; the library allocates no memory
+ *     and keeps no per-call state.
+ *   - BF16 tensors are passed as raw 16-bit patterns, E4M3 tensors as bytes.
+ *   - Shapes: K (and N) must be multiples of 128; M >= 0 (M == 0 is a no-op).
+ *   - Alignment: BF16 and E4M3 tensors 16-byte aligned, FP32 scale tensors 4-byte
+ *     aligned.
+ *   - Calls only enqueue work on `stream` (NULL = the device's null stream) and
+ *     never synchronize.  Validation happens on the host before any launch and is
+ *     reported synchronously; a fault inside a kernel surfaces at the caller's
+ *     next synchronization, as for any HIP library.
+ *   - Inputs must be finite.  NaN or infinity in an input is outside the contract.
+ *   - Return value: FP8BS_OK (0) or a negative fp8bs_status code.
+ *   - The device must be gfx950; other devices get FP8BS_ERR_DEVICE.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP8BS_OK = 0,
+    FP8BS_ERR_NULL = -1,      /* a required pointer is NULL                       */
+    FP8BS_ERR_SHAPE = -2,     /* negative size, K or N not a multiple of 128, or  */
+                              /* an index range that overflows int64            */
+    FP8BS_ERR_ALIGN = -3,     /* a pointer violates the alignment rule above      */
+    FP8BS_ERR_DEVICE = -4,    /* the current device is not gfx950                 */
+    FP8BS_ERR_HIP = -5,       /* a HIP runtime call or a kernel launch failed     */
+    FP8BS_ERR_WORKSPACE = -6  /* workspace given but misaligned                   */
+} fp8bs_status;
+
+/*
+ * Dynamic per-token, group-128 activation quantization.
+ *   x_bf16 [M, K]      BF16 input (in).
+ *   q_e4m3 [M, K]      E4M3 codes (out).
+ *   s_f32  [M, K/128]  scales (out); s[m, g] covers x[m, 128 g .. 128 g + 127].
+ * For every group: s = fl32(amax / 448) with amax the largest |x| of the group
+ * (IEEE float32 division, round to nearest even, subnormals kept);
+ * q = E4M3(fl32(x / s)) rounded to nearest even and saturated at +-448.  A group
+ * whose amax is 0 gets s = +0.0 and codes 0x00.  Bit-exact and deterministic.
+ */
+int fp8_quant_act(const void* x_bf16, void* q_e4m3, float* s_f32,
+                  int64_t M, int64_t K, hipStream_t stream);
+
+/*
+ * 128x128 block weight quantization (offline step; same rounding as above).
+ *   w_bf16  [N, K]            BF16 weights, row n = output channel n (in).
+ *   qw_e4m3 [N, K]            E4M3 codes (out).
+ *   ws_f32  [N/128, K/128]    scales (out); ws[i, j] covers rows 128 i .. 128 i + 127
+ *                             and columns 128 j .. 128 j + 127.
+ * N and K must be multiples of 128.
+ */
+int fp8_quant_weight(const void* w_bf16, void* qw_e4m3, float* ws_f32,
+                     int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * Input of the down projection: h = BF16(silu(gate) * up), then the activation
+ * quantization above applied to h.
+ *   gu_bf16 [M, 2 I]    fused gate/up output: gate = columns [0, I), up = [I, 2 I).
+ *   q_e4m3  [M, I]      E4M3 codes of h (out).
+ *   s_f32   [M, I/128]  scales of h (out).
+ * silu(g) = g / (1 + exp(-g)); the product is evaluated in FP64 and rounded to
+ * BF16 once (nearest even).  I must be a multiple of 128.
+ */
+int fp8_silu_mul_quant(const void* gu_bf16, void* q_e4m3, float* s_f32,
+                       int64_t M, int64_t I, hipStream_t stream);
+
+/*
+ * Block-scaled FP8 GEMM: y = (q * s) @ (w * ws)^T, accumulated in FP32, stored BF16.
+ *   q_e4m3  [M, K]            activation codes; s_f32 [M, K/128] their scales.
+ *   w_e4m3  [N, K]            weight codes;     ws_f32 [N/128, K/128] block scales.
+ *   y_bf16  [M, N]            output (out), rounded to BF16 (nearest even) once.
+ *   workspace / workspace_bytes
+ *       Scratch for the split-K / stream-K schedule used when M <= 16: FP32
+ *       partial sums and per-strip arrival counters.  Size it with
+ *       fp8_block_linear_workspace_size.  It must be zero-filled before its first
+ *       use; every call that completes resets the counters it used to zero, so one
+ *       buffer serves consecutive calls on one stream without clearing.  Two calls
+ *       that may run at the same time must not share a workspace.  NULL, or fewer
+ *       bytes than required, selects a schedule without split-K (slower, same
+ *       accuracy contract).  Must be 256-byte aligned when given.
+ * Per 128-wide K block the FP32 partial product is multiplied by s[m, kb] *
+ * ws[n/128, kb] and added to an FP32 accumulator.  The summation order is fixed
+ * for a given (M, N, K, device, workspace size), so repeated calls give
+ * bitwise-identical outputs.  Accuracy: |y - ref| <= 4e-3 |ref| + 1e-3 rms(ref)
+ * against the exact dequantize-and-matmul.
+ */
+int fp8_block_linear(const void* q_e4m3, const float* s_f32,
+                     const void* w_e4m3, const float* ws_f32,
+                     void* y_bf16, int64_t M, int64_t N, int64_t K,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace the fastest schedule of fp8_block_linear needs (0 if none).
+ * Returns 0 for invalid shapes as well. */
+size_t fp8_block_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* Static, human-readable text for a status code. */
+const char* fp8bs_status_string(int status);
+
+/* ABI version of this header: major * 10000 + minor * 100 + patch. */
+int fp8bs_abi_version(void);
+
+#define FP8BS_ABI_VERSION 10000
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

@@ -1,0 +1,97 @@
+"""The C ABI library loads, exports every symbol include/fp8bs.h declares, and rejects
+bad arguments on the host before any GPU work (no compute calls are made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp8_block_scaled_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+
+OK, ENULL, ESHAPE, EALIGN, EDEV, EHIP, EWS = 0, -1, -2, -3, -4, -5, -6
+# Fake, never-dereferenced addresses: validation must reject before using them.
+A16, A16b, A16c, A16d, A16e = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s*(fp8\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert {"fp8_quant_act", "fp8_block_linear"} <= set(names)
+    assert set(names) == set(_lib.SIGNATURES), names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert L.fp8bs_abi_version() == 10000
+    for st in (OK, ENULL, ESHAPE, EALIGN, EDEV, EHIP, EWS):
+        assert L.fp8bs_status_string(st)
+    assert b"unknown" in L.fp8bs_status_string(12345)
+
+
+def test_quant_act_validation(L):
+    assert L.fp8_quant_act(None, A16, A16b, 4, 128, None) == ENULL
+    assert L.fp8_quant_act(A16, A16b, A16c, 4, 200, None) == ESHAPE
+    assert L.fp8_quant_act(A16, A16b, A16c, -1, 128, None) == ESHAPE
+    assert L.fp8_quant_act(A16, A16b, A16c, 1 << 40, 1 << 40, None) == ESHAPE
+    assert L.fp8_quant_act(A16 + 2, A16b, A16c, 4, 128, None) == EALIGN
+    assert L.fp8_quant_act(A16, A16b + 8, A16c, 4, 128, None) == EALIGN
+    assert L.fp8_quant_act(A16, A16b, A16c + 2, 4, 128, None) == EALIGN
+    assert L.fp8_quant_act(None, None, None, 0, 128, None) == OK      # empty: no-op
+
+
+def test_weight_and_silu_validation(L):
+    assert L.fp8_quant_weight(A16, A16b, A16c, 100, 128, None) == ESHAPE
+    assert L.fp8_quant_weight(A16, A16b, A16c, 128, 100, None) == ESHAPE
+    assert L.fp8_quant_weight(None, A16b, A16c, 128, 128, None) == ENULL
+    assert L.fp8_silu_mul_quant(A16, A16b, A16c, 2, 100, None) == ESHAPE
+    assert L.fp8_silu_mul_quant(A16, None, A16c, 2, 128, None) == ENULL
+    assert L.fp8_silu_mul_quant(A16, A16b, A16c, 0, 128, None) == OK
+
+
+def test_block_linear_validation(L):
+    f = L.fp8_block_linear
+    assert f(A16, A16b, A16c, A16d, A16e, 4, 100, 128, None, 0, None) == ESHAPE
+    assert f(A16, A16b, A16c, A16d, A16e, 4, 128, 100, None, 0, None) == ESHAPE
+    assert f(A16, A16b, A16c, A16d, A16e, 4, 128, 0, None, 0, None) == ESHAPE
+    assert f(A16, A16b, A16c, A16d, A16e, -4, 128, 128, None, 0, None) == ESHAPE
+    assert f(None, A16b, A16c, A16d, A16e, 4, 128, 128, None, 0, None) == ENULL
+    assert f(A16, A16b, A16c, A16d, None, 4, 128, 128, None, 0, None) == ENULL
+    assert f(A16 + 4, A16b, A16c, A16d, A16e, 4, 128, 128, None, 0, None) == EALIGN
+    assert f(A16, A16b + 1, A16c, A16d, A16e, 4, 128, 128, None, 0, None) == EALIGN
+    assert f(A16, A16b, A16c, A16d, A16e + 8, 4, 128, 128, None, 0, None) == EALIGN
+    assert f(A16, A16b, A16c, A16d, A16e, 4, 128, 128, A16 + 16, 4096, None) == EWS
+    assert f(None, None, None, None, None, 0, 128, 128, None, 0, None) == OK     # M == 0
+    assert f(None, None, None, None, None, 4, 0, 128, None, 0, None) == OK       # N == 0
+
+
+def test_valid_call_without_a_gpu_reports_a_hip_error_not_a_crash(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert L.fp8_quant_act(A16, A16b, A16c, 4, 128, None) in (EHIP, EDEV)
+
+
+def test_workspace_size_is_zero_for_prefill_and_invalid_shapes(L):
+    assert L.fp8_block_linear_workspace_size(8191, 7168, 7168) == 0
+    assert L.fp8_block_linear_workspace_size(4, 100, 128) == 0
+    assert L.fp8_block_linear_workspace_size(-1, 128, 128) == 0
+    ws = L.fp8_block_linear_workspace_size(1, 9216, 7168)
+    assert ws > 0 and ws % 256 == 0

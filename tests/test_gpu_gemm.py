@@ -1,0 +1,146 @@
+"""GPU parity: the HIP block-scaled GEMM against the float64 oracle.
+
+Every element must satisfy |y - ref| <= 4e-3 |ref| + 1e-3 rms(ref).  Special cases
+whose result is exact are compared bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_amd as fb
+import oracle
+import synth
+from tests.gpu_util import assert_bits_equal, banner, dev_bf16, dev_f32, dev_u8, host_u16
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16(x):
+    x = np.asarray(x, dtype=np.float32)
+    return synth.f32_to_bf16_bits(x).reshape(x.shape)
+
+
+def inputs(M, N, K, seed, x_sigma=1.0, w_sigma=0.02):
+    """Seeded BF16 activations [M, K] and weights [N, K] (host bit patterns)."""
+    rng = np.random.default_rng(seed)
+    return bf16(rng.standard_normal((M, K)) * x_sigma), bf16(rng.standard_normal((N, K)) * w_sigma)
+
+
+def gpu_path(x, w, workspace=None, ws_mult=None):
+    """The HIP path end to end: quantize both operands on the GPU, then the GEMM."""
+    q, s = fb.quant_act(dev_bf16(x))
+    qw, ws = fb.quant_weight(dev_bf16(w))
+    if ws_mult is not None:
+        ws = ws * ws_mult
+    y = fb.block_linear(q, s, qw, ws, workspace=workspace)
+    torch.cuda.synchronize()
+    return host_u16(y)
+
+
+def oracle_path(x, w):
+    q, s = oracle.quant_act(x)
+    qw, ws = oracle.quant_weight(w)
+    return oracle.linear_ref(q, s, qw, ws)
+
+
+def check_linear(x, w, what, workspace=None):
+    banner(f"block_linear {what} M={x.shape[0]} N={w.shape[0]} K={x.shape[1]}")
+    y = gpu_path(x, w, workspace)
+    res = oracle.check_tolerance(y, oracle_path(x, w))
+    assert res["ok"], f"{what}: {res}"
+    return y
+
+
+SHAPES = [(M, N, K) for M in (1, 2, 5, 8, 9, 16, 17, 33, 100, 128, 129, 255, 300)
+          for (N, K) in ((128, 128), (384, 512), (1024, 1152))]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_linear_shapes(M, N, K):
+    x, w = inputs(M, N, K, seed=M * 31 + N + K)
+    check_linear(x, w, "random")
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 40, 200])
+def test_linear_without_workspace(M):
+    x, w = inputs(M, 1152, 2048, seed=M)
+    check_linear(x, w, "no workspace", workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+
+
+@pytest.mark.parametrize("M", [3, 8, 16, 64, 200])
+def test_identity_weights_bitwise(M):
+    """s = 1 (every group holds 448) and identity weights: y = dec(q) exactly."""
+    rng = np.random.default_rng(M)
+    x = bf16(rng.standard_normal((M, 128)) * 60.0)
+    x[:, 5] = bf16(np.float32(448.0))
+    qg, sg = fb.quant_act(dev_bf16(x))
+    qw = np.zeros((128, 128), np.uint8)
+    np.fill_diagonal(qw, 0x38)                       # E4M3 1.0 on the diagonal
+    y = fb.block_linear(qg, sg, dev_u8(qw), dev_f32(np.ones((1, 1), np.float32)))
+    torch.cuda.synchronize()
+    y = host_u16(y)
+    q, s = oracle.quant_act(x)
+    assert np.all(s == 1.0)
+    want = bf16(oracle.decode(q).astype(np.float32))
+    zero = (want & 0x7FFF) == 0
+    assert_bits_equal(np.where(zero, 0, y), np.where(zero, 0, want), "identity")
+    assert np.all((y[zero] & 0x7FFF) == 0)
+
+
+@pytest.mark.parametrize("M", [4, 16, 129])
+def test_zero_tokens_exact_zero(M):
+    x, w = inputs(M, 384, 512, seed=5)
+    x[1] = 0
+    y = gpu_path(x, w)
+    assert np.all(y[1] == 0)                 # +0.0 exactly
+    assert np.all(np.any(y[[0, 2]] != 0, axis=1))
+
+
+@pytest.mark.parametrize("M", [1, 8, 100])
+def test_negation_symmetry(M):
+    x, w = inputs(M, 1024, 1152, seed=9)
+    y = gpu_path(x, w).astype(np.uint32)
+    yn = gpu_path(x ^ np.uint16(0x8000), w).astype(np.uint32)
+    f = lambda b: (b << 16).view(np.float32)
+    assert np.array_equal(f(yn), -f(y))
+
+
+@pytest.mark.parametrize("M", [1, 8, 64])
+def test_power_of_two_weight_scale_doubles_output(M):
+    x, w = inputs(M, 384, 1152, seed=10)
+    y = gpu_path(x, w)
+    y2 = gpu_path(x, w, ws_mult=2.0)
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(f(y2), 2 * f(y))
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 300])
+def test_deterministic(M):
+    x, w = inputs(M, 2048, 3072, seed=11)
+    args = (*fb.quant_act(dev_bf16(x)), *fb.quant_weight(dev_bf16(w)))
+    ref = fb.block_linear(*args).clone()
+    for _ in range(5):
+        assert torch.equal(fb.block_linear(*args), ref)
+
+
+def test_workspace_reused_across_calls():
+    """One zero-filled workspace serves consecutive split-K calls of different shapes."""
+    need = max(fb.workspace_size(M, N, K) for (M, N, K) in ((1, 9216, 7168), (8, 7168, 8192), (3, 384, 512)))
+    assert need > 0
+    wsp = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (M, N, K) in enumerate(((1, 9216, 7168), (8, 7168, 8192), (3, 384, 512), (1, 9216, 7168))):
+        x, w = inputs(M, N, K, seed=40 + i)
+        check_linear(x, w, f"shared workspace call {i}", workspace=wsp)
+
+
+def test_subnormal_codes_and_scales():
+    """E4M3 subnormal codes and FP32-subnormal scales reach the MFMA and the promotion."""
+    rng = np.random.default_rng(13)
+    M, N, K = 8, 256, 256
+    x = bf16(rng.standard_normal((M, K)) * 1e-3)
+    x[:, ::2] = bf16(rng.standard_normal((M, K // 2)) * 1e-6)    # tiny -> subnormal codes
+    x[0] = bf16(rng.standard_normal(K) * 1e-39)                   # subnormal scales
+    w = bf16(rng.standard_normal((N, K)) * 0.02)
+    q, s = oracle.quant_act(x)
+    assert np.any((q & 0x78) == 0) and np.any(s < np.finfo(np.float32).tiny)
+    check_linear(x, w, "subnormal codes")

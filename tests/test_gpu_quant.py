@@ -1,0 +1,119 @@
+"""GPU parity: the HIP quantizers against the CPU oracle, bit for bit.
+
+Codes and scales must match exactly (activations: per-token group-128; weights:
+128x128 blocks; SiLU(gate)*up re-quantization)."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_amd as fb
+import oracle
+import synth
+from tests.gpu_util import assert_bits_equal, banner, dev_bf16, host_f32, host_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16(x):
+    x = np.asarray(x, dtype=np.float32)
+    return synth.f32_to_bf16_bits(x).reshape(x.shape)
+
+
+def run_quant(bits):
+    q, s = fb.quant_act(dev_bf16(bits))
+    torch.cuda.synchronize()
+    return host_u8(q), host_f32(s)
+
+
+def check_quant(bits, what):
+    banner(f"quant_act {what} shape={bits.shape}")
+    q, s = run_quant(bits)
+    qo, so = oracle.quant_act(bits)
+    assert_bits_equal(s, so, f"{what} scales")
+    assert_bits_equal(q, qo, f"{what} codes")
+
+
+@pytest.mark.parametrize("M,K,sigma", [(1, 128, 1.0), (3, 384, 0.02), (4, 512, 1.0), (17, 1024, 7.0),
+                                       (64, 7168, 1.0), (129, 2048, 1e-3), (1000, 256, 3e4)])
+def test_quant_act_random(M, K, sigma):
+    rng = np.random.default_rng(M * 1000 + K)
+    check_quant(bf16(rng.standard_normal((M, K)) * sigma), f"random sigma={sigma}")
+
+
+def test_quant_act_edge_groups():
+    rng = np.random.default_rng(7)
+    x = bf16(rng.standard_normal((12, 1024)))
+    x[0, :128] = 0                         # +0 group
+    x[1, :] = 0x8000                       # row of -0.0
+    x[2, :128] = 0x0001                    # smallest subnormal everywhere
+    x[2, 128:256] = 0x8001
+    x[2, 256:384] = bf16(np.full(128, 3.0))        # constant group -> all 448
+    x[3, :128] = 0x7F7F                    # largest finite BF16
+    x[3, 128] = 0xFF7F
+    x[4, :] = bf16(rng.standard_normal(1024) * 1e-38)   # subnormal scales
+    x[5, 0] = bf16(np.float32(448.0))      # s = 1: x/s = x, codes hit E4M3 midpoints
+    mids = []
+    t = oracle.decode_table()[:0x7F]
+    for c in range(0x7E):
+        mids.append((t[c] + t[c + 1]) / 2)
+    mids = np.array(mids, dtype=np.float32)          # the 126 midpoints between magnitudes
+    x[5, 1:127] = bf16(mids)
+    x[5, 128:256] = bf16(-np.float32(448.0) * np.ones(128))
+    x[6, 1:128] = bf16(np.float32(1e-30))  # one non-zero in a group of tiny values
+    x[6, 0] = bf16(np.float32(5.0))
+    x[7, :] = bf16(np.linspace(-448, 448, 1024))
+    x[8, ::2] = 0x8000
+    check_quant(x, "edge groups")
+
+
+def test_quant_act_every_bf16_amax():
+    """One group per positive finite BF16 amax (32639 groups), the other 127 values
+    spread over [-amax, amax] in BF16."""
+    amax_bits = np.arange(1, 0x7F80, dtype=np.uint32)
+    amax = (amax_bits << 16).view(np.float32)
+    frac = np.linspace(-1.0, 1.0, 127, dtype=np.float64)
+    body = (amax[:, None].astype(np.float64) * frac[None, :]).astype(np.float32)
+    # |amax * frac| <= amax and amax is a BF16 value, so rounding never exceeds it.
+    x = np.concatenate([amax_bits.astype(np.uint16)[:, None], bf16(body)], axis=1)
+    check_quant(np.ascontiguousarray(x), "all BF16 amax values")
+
+
+def test_quant_act_empty():
+    q, s = fb.quant_act(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"))
+    assert q.shape == (0, 256) and s.shape == (0, 2)
+
+
+@pytest.mark.parametrize("N,K,sigma", [(128, 128, 0.02), (384, 512, 0.02), (256, 1152, 10.0), (1024, 256, 1e-5)])
+def test_quant_weight_random(N, K, sigma):
+    rng = np.random.default_rng(N + K)
+    w = bf16(rng.standard_normal((N, K)) * sigma)
+    w[:128, :128] = 0                      # an all-zero block
+    banner(f"quant_weight N={N} K={K}")
+    qw, ws = fb.quant_weight(dev_bf16(w))
+    torch.cuda.synchronize()
+    qo, so = oracle.quant_weight(w)
+    assert_bits_equal(host_f32(ws), so, "weight scales")
+    assert_bits_equal(host_u8(qw), qo, "weight codes")
+
+
+@pytest.mark.parametrize("M,I,sigma", [(1, 128, 1.7), (8, 8192, 1.7), (37, 1024, 0.3), (5, 256, 40.0)])
+def test_silu_mul_quant(M, I, sigma):
+    rng = np.random.default_rng(M * 7 + I)
+    gu = bf16(rng.standard_normal((M, 2 * I)) * sigma)
+    gu[0, :8] = bf16(np.array([0, -0.0, 80, -80, 1e-30, -1e-30, 300, -300], np.float32))
+    banner(f"silu_mul_quant M={M} I={I}")
+    q, s = fb.silu_mul_quant(dev_bf16(gu))
+    torch.cuda.synchronize()
+    qo, so = oracle.silu_mul_quant(gu)
+    assert_bits_equal(host_f32(s), so, "silu scales")
+    assert_bits_equal(host_u8(q), qo, "silu codes")
+
+
+def test_quant_is_deterministic():
+    rng = np.random.default_rng(99)
+    x = dev_bf16(bf16(rng.standard_normal((257, 2048))))
+    ref = [t.clone() for t in fb.quant_act(x)]
+    for _ in range(3):
+        q, s = fb.quant_act(x)
+        assert torch.equal(q, ref[0]) and torch.equal(s.view(torch.int32), ref[1].view(torch.int32))
