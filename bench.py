@@ -11,9 +11,11 @@ whose metric is achieved GB/s: its weight stream is 99.9% of its bytes.  Inputs
 are resident in HBM before timing; weight copies are rotated so that the weights
 touched between two uses of one copy exceed twice the 256 MB Infinity Cache.
 
-Timing: W untimed warm-up steps, then K steps bracketed by device synchronization.
-Each launch of the dominant kernel (the GEMM) is bracketed by HIP events on the
-stream it runs on, giving its average duration for the roofline.
+Timing: W untimed warm-up steps, then K steps bracketed by device synchronization,
+run as one replay of a HIP graph holding the K steps (the host's launch cost stays
+out of the device timeline).  The dominant kernel (the GEMM) is also captured
+alone, K launches, and replayed between HIP events on the stream it runs on,
+giving its average duration for the roofline.
 
 Printed: ONE JSON line.  Besides the contract fields it carries the other
 workloads' numbers ("workloads"), measured the same way.
@@ -106,32 +108,47 @@ class Case:
         fb.block_linear(self.q, self.s, self.qw[c], self.ws[c], out=self.y, workspace=self.workspace)
 
 
+def _replay_ms(graph):
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
 def time_case(case, steps, warmup):
-    """Run warmup + timed steps; return (ms per step, avg GEMM us, avg quant us)."""
+    """W eager warm-up steps, then K steps timed as one replay of a HIP graph that
+    holds them (so host launch cost is not in the measurement).  The GEMM and the
+    quantizer are also captured alone, K launches each, for their average duration
+    on the stream they run on.  Returns (ms per step, GEMM us, quant us)."""
     import torch
     for i in range(warmup):
         case.quant()
         case.gemm(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    g_step, g_gemm, g_quant = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step):
+        for i in range(steps):
+            case.quant()
+            case.gemm(i)
+    with torch.cuda.graph(g_gemm):
+        for i in range(steps):
+            case.gemm(i)
+    with torch.cuda.graph(g_quant):
+        for i in range(steps):
+            case.quant()
+    for g in (g_step, g_gemm, g_quant):     # untimed replay: first-replay costs
+        g.replay()
     torch.cuda.synchronize()
-    t_start.record()
-    for i in range(steps):
-        e0, e1, e2 = ev[i]
-        e0.record()
-        case.quant()
-        e1.record()
-        case.gemm(i)
-        e2.record()
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    quant_us = sum(a.elapsed_time(b) for a, b, _ in ev) * 1e3 / steps
-    gemm_us = sum(b.elapsed_time(c) for _, b, c in ev) * 1e3 / steps
-    return total_ms / steps, gemm_us, quant_us
+    ms_step = _replay_ms(g_step) / steps
+    gemm_us = _replay_ms(g_gemm) * 1e3 / steps
+    quant_us = _replay_ms(g_quant) * 1e3 / steps
+    del g_step, g_gemm, g_quant
+    return ms_step, gemm_us, quant_us
 
 
 def roofline_for(wl, gemm_us, traffic):

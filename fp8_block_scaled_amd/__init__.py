@@ -31,12 +31,14 @@ __all__ = [
 _workspaces = {}
 
 
-def _stream(device):
-    return ctypes_stream(torch.cuda.current_stream(device))
-
-
-def ctypes_stream(stream):
-    return stream.cuda_stream
+def _call(fn_name, device, *args):
+    """Call a C entry point with the current stream of ``device`` appended."""
+    fn = getattr(lib(), fn_name)
+    if device.index is None or device.index == torch.cuda.current_device():
+        check(fn_name, fn(*args, torch.cuda.current_stream().cuda_stream))
+    else:
+        with torch.cuda.device(device):
+            check(fn_name, fn(*args, torch.cuda.current_stream().cuda_stream))
 
 
 def _check_tensor(t, name, dtypes, ndim):
@@ -62,8 +64,7 @@ def quant_act(x, q=None, s=None):
     M, K = x.shape
     q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
     s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if s is None else s
-    with torch.cuda.device(x.device):
-        check("fp8_quant_act", lib().fp8_quant_act(x.data_ptr(), q.data_ptr(), s.data_ptr(), M, K, _stream(x.device)))
+    _call("fp8_quant_act", x.device, x.data_ptr(), q.data_ptr(), s.data_ptr(), M, K)
     return q, s
 
 
@@ -73,9 +74,7 @@ def quant_weight(w):
     N, K = w.shape
     qw = torch.empty((N, K), dtype=torch.uint8, device=w.device)
     ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
-    with torch.cuda.device(w.device):
-        check("fp8_quant_weight",
-              lib().fp8_quant_weight(w.data_ptr(), qw.data_ptr(), ws.data_ptr(), N, K, _stream(w.device)))
+    _call("fp8_quant_weight", w.device, w.data_ptr(), qw.data_ptr(), ws.data_ptr(), N, K)
     return qw, ws
 
 
@@ -88,9 +87,7 @@ def silu_mul_quant(gu, q=None, s=None):
     I = two_i // 2
     q = torch.empty((M, I), dtype=torch.uint8, device=gu.device) if q is None else q
     s = torch.empty((M, I // 128), dtype=torch.float32, device=gu.device) if s is None else s
-    with torch.cuda.device(gu.device):
-        check("fp8_silu_mul_quant",
-              lib().fp8_silu_mul_quant(gu.data_ptr(), q.data_ptr(), s.data_ptr(), M, I, _stream(gu.device)))
+    _call("fp8_silu_mul_quant", gu.device, gu.data_ptr(), q.data_ptr(), s.data_ptr(), M, I)
     return q, s
 
 
@@ -135,8 +132,6 @@ def block_linear(q, s, qw, ws, out=None, workspace=None):
         workspace = get_workspace(dev, need) if need else None
     wptr = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    with torch.cuda.device(dev):
-        check("fp8_block_linear",
-              lib().fp8_block_linear(q.data_ptr(), s.data_ptr(), qw.data_ptr(), ws.data_ptr(), y.data_ptr(),
-                                     M, N, K, wptr, wbytes, _stream(dev)))
+    _call("fp8_block_linear", dev, q.data_ptr(), s.data_ptr(), qw.data_ptr(), ws.data_ptr(), y.data_ptr(),
+          M, N, K, wptr, wbytes)
     return y

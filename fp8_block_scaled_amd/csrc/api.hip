@@ -95,10 +95,8 @@ int fp8_silu_mul_quant(const void* gu_bf16, void* q_e4m3, float* s_f32, int64_t 
 size_t fp8_block_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K <= 0 || N % 128 || K % 128 || !mul_ok(N, K) || !mul_ok(M, K) || !mul_ok(M, N))
         return 0;
-    if (M == 0 || N == 0 || M > fp8bs::kDecodeMaxM) return 0;
-    int cus = 256;
-    if (check_device(&cus) != FP8BS_OK) cus = 256;
-    return fp8bs::decode_workspace_bytes(fp8bs::plan_decode(M, N, K, cus, true));
+    // No current schedule needs scratch memory; the argument is kept in the ABI.
+    return 0;
 }
 
 int fp8_block_linear(const void* q_e4m3, const float* s_f32, const void* w_e4m3, const float* ws_f32,
@@ -115,12 +113,11 @@ int fp8_block_linear(const void* q_e4m3, const float* s_f32, const void* w_e4m3,
     int cus = 0;
     int rc = check_device(&cus);
     if (rc != FP8BS_OK) return rc;
+    (void)workspace_bytes;
     if (M <= fp8bs::kDecodeMaxM) {
-        fp8bs::DecodePlan plan = fp8bs::plan_decode(M, N, K, cus, true);
-        if (plan.split && (!workspace || workspace_bytes < fp8bs::decode_workspace_bytes(plan)))
-            plan = fp8bs::plan_decode(M, N, K, cus, false);
+        const fp8bs::DecodePlan plan = fp8bs::plan_decode(M, N, K, cus);
         return hip_status(
-            fp8bs::launch_gemm_decode(plan, q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, workspace, stream));
+            fp8bs::launch_gemm_decode(plan, q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, stream));
     }
     return hip_status(fp8bs::launch_gemm_prefill(q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, cus, stream));
 }

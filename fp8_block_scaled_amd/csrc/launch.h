@@ -12,29 +12,19 @@ hipError_t launch_quant_act(const void* x, void* q, float* s, int64_t M, int64_t
 hipError_t launch_silu_mul_quant(const void* gu, void* q, float* s, int64_t M, int64_t I, hipStream_t st);
 hipError_t launch_quant_weight(const void* w, void* qw, float* ws, int64_t N, int64_t K, hipStream_t st);
 
-// ---- decode GEMM (M <= kDecodeMaxM): stream-K over (16-column strip, K block) units
+// ---- decode GEMM (M <= kDecodeMaxM): one workgroup per 16-column strip, split-K over its waves
 constexpr int kDecodeMaxM = 16;
 
 struct DecodePlan {
-    int64_t strips;      // N / 16
+    int64_t strips;      // N / 16: workgroups
     int64_t kblocks;     // K / 128
-    int64_t units;       // strips * kblocks
-    int64_t workers;     // waves; worker w owns units [w*base + min(w,rem), +base + (w<rem))
-    int64_t base, rem;
-    int64_t max_contrib; // partial slots per strip
-    size_t part_bytes;   // strips * max_contrib * 1 KiB
-    size_t cnt_bytes;    // fixed counter region (only when split)
-    bool split;          // some strip is shared by several workers
+    int waves;           // waves per workgroup = K splits
 };
 
-// Plan for a device with `cus` compute units.  `allow_split` false gives one worker
-// per strip (no workspace).
-DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int cus, bool allow_split);
-size_t decode_workspace_bytes(const DecodePlan& p);
+DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int cus);
 
 hipError_t launch_gemm_decode(const DecodePlan& plan, const void* q, const float* s, const void* w,
-                              const float* ws, void* y, int64_t M, int64_t N, int64_t K,
-                              void* workspace, hipStream_t st);
+                              const float* ws, void* y, int64_t M, int64_t N, int64_t K, hipStream_t st);
 
 // ---- prefill GEMM (M > kDecodeMaxM): LDS-tiled FP8 MFMA
 hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, const float* ws, void* y,

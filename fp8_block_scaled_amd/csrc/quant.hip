@@ -20,9 +20,10 @@
 namespace fp8bs {
 
 constexpr int kQuantThreads = 256;           // 16 groups per block pass
-constexpr int kQuantUnroll = 4;              // groups per 16-lane row per block
-
-struct Bf16x8 { uint4 v; };
+// Groups per 16-lane row: 4 for large inputs (more loads in flight per lane), 1
+// when the input is too small to fill the GPU otherwise.
+constexpr int kQuantUnrollBig = 4;
+constexpr int64_t kSmallGroups = 16 * 4 * 1024;
 
 __device__ __forceinline__ void unpack8(const uint4& v, float (&x)[8]) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -57,6 +58,7 @@ __device__ __forceinline__ float absmax8(const float (&x)[8]) {
 }
 
 // Groups [blockIdx.x * 16 * U, +16 * U): pass u handles groups base + 16 u + row.
+template <int kQuantUnroll>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ s, int64_t n_groups) {
     const int row = threadIdx.x >> 4;
@@ -84,6 +86,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
 
 // gu [M, 2I]: gate = columns [0, I), up = [I, 2I).  Group g of h: row g / (I/128),
 // columns 128 (g % (I/128)) + [0, 128).
+template <int kQuantUnroll>
 __global__ __launch_bounds__(kQuantThreads) void silu_mul_quant_kernel(
     const uint16_t* __restrict__ gu, uint8_t* __restrict__ q, float* __restrict__ s,
     int64_t n_groups, int64_t groups_per_row, int64_t I) {
@@ -154,10 +157,14 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(
 hipError_t launch_quant_act(const void* x, void* q, float* s, int64_t M, int64_t K, hipStream_t st) {
     const int64_t n_groups = M * (K / kGroup);
     if (n_groups == 0) return hipSuccess;
-    const int64_t per_block = 16 * kQuantUnroll;
-    const int64_t blocks = (n_groups + per_block - 1) / per_block;
-    hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0, st,
-                       (const uint16_t*)x, (uint8_t*)q, s, n_groups);
+    if (n_groups < kSmallGroups) {
+        hipLaunchKernelGGL(quant_act_kernel<1>, dim3((unsigned)((n_groups + 15) / 16)), dim3(kQuantThreads), 0, st,
+                           (const uint16_t*)x, (uint8_t*)q, s, n_groups);
+    } else {
+        const int64_t per_block = 16 * kQuantUnrollBig;
+        hipLaunchKernelGGL(quant_act_kernel<kQuantUnrollBig>, dim3((unsigned)((n_groups + per_block - 1) / per_block)),
+                           dim3(kQuantThreads), 0, st, (const uint16_t*)x, (uint8_t*)q, s, n_groups);
+    }
     return hipGetLastError();
 }
 
@@ -165,10 +172,15 @@ hipError_t launch_silu_mul_quant(const void* gu, void* q, float* s, int64_t M, i
     const int64_t gpr = I / kGroup;
     const int64_t n_groups = M * gpr;
     if (n_groups == 0) return hipSuccess;
-    const int64_t per_block = 16 * kQuantUnroll;
-    const int64_t blocks = (n_groups + per_block - 1) / per_block;
-    hipLaunchKernelGGL(silu_mul_quant_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0, st,
-                       (const uint16_t*)gu, (uint8_t*)q, s, n_groups, gpr, I);
+    if (n_groups < kSmallGroups) {
+        hipLaunchKernelGGL(silu_mul_quant_kernel<1>, dim3((unsigned)((n_groups + 15) / 16)), dim3(kQuantThreads), 0,
+                           st, (const uint16_t*)gu, (uint8_t*)q, s, n_groups, gpr, I);
+    } else {
+        const int64_t per_block = 16 * kQuantUnrollBig;
+        hipLaunchKernelGGL(silu_mul_quant_kernel<kQuantUnrollBig>,
+                           dim3((unsigned)((n_groups + per_block - 1) / per_block)), dim3(kQuantThreads), 0, st,
+                           (const uint16_t*)gu, (uint8_t*)q, s, n_groups, gpr, I);
+    }
     return hipGetLastError();
 }
 

@@ -88,14 +88,11 @@ int fp8_silu_mul_quant(const void* gu_bf16, void* q_e4m3, float* s_f32,
  *   w_e4m3  [N, K]            weight codes;     ws_f32 [N/128, K/128] block scales.
  *   y_bf16  [M, N]            output (out), rounded to BF16 (nearest even) once.
  *   workspace / workspace_bytes
- *       Scratch for the split-K / stream-K schedule used when M <= 16: FP32
- *       partial sums and per-strip arrival counters.  Size it with
- *       fp8_block_linear_workspace_size.  It must be zero-filled before its first
- *       use; every call that completes resets the counters it used to zero, so one
- *       buffer serves consecutive calls on one stream without clearing.  Two calls
- *       that may run at the same time must not share a workspace.  NULL, or fewer
- *       bytes than required, selects a schedule without split-K (slower, same
- *       accuracy contract).  Must be 256-byte aligned when given.
+ *       Optional device scratch for schedules that need it, sized by
+ *       fp8_block_linear_workspace_size.  The current schedules need none (the
+ *       decode schedule reduces its split-K partial sums inside each workgroup), so
+ *       the size query returns 0 and NULL / 0 may be passed.  When given it must be
+ *       256-byte aligned; a workspace that is too small never causes an error.
  * Per 128-wide K block the FP32 partial product is multiplied by s[m, kb] *
  * ws[n/128, kb] and added to an FP32 accumulator.  The summation order is fixed
  * for a given (M, N, K, device, workspace size), so repeated calls give
@@ -107,8 +104,9 @@ int fp8_block_linear(const void* q_e4m3, const float* s_f32,
                      void* y_bf16, int64_t M, int64_t N, int64_t K,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace the fastest schedule of fp8_block_linear needs (0 if none).
- * Returns 0 for invalid shapes as well. */
+/* Bytes of workspace the fastest schedule of fp8_block_linear needs for this shape
+ * (0 if none, which is the case for every shape in this version; 0 for invalid
+ * shapes as well). */
 size_t fp8_block_linear_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /* Static, human-readable text for a status code. */

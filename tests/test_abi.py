@@ -89,9 +89,6 @@ def test_valid_call_without_a_gpu_reports_a_hip_error_not_a_crash(L):
     assert L.fp8_quant_act(A16, A16b, A16c, 4, 128, None) in (EHIP, EDEV)
 
 
-def test_workspace_size_is_zero_for_prefill_and_invalid_shapes(L):
-    assert L.fp8_block_linear_workspace_size(8191, 7168, 7168) == 0
-    assert L.fp8_block_linear_workspace_size(4, 100, 128) == 0
-    assert L.fp8_block_linear_workspace_size(-1, 128, 128) == 0
-    ws = L.fp8_block_linear_workspace_size(1, 9216, 7168)
-    assert ws > 0 and ws % 256 == 0
+def test_workspace_size_query(L):
+    for shape in ((8191, 7168, 7168), (4, 100, 128), (-1, 128, 128), (1, 9216, 7168), (8, 7168, 8192)):
+        assert L.fp8_block_linear_workspace_size(*shape) == 0

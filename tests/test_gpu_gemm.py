@@ -123,14 +123,29 @@ def test_deterministic(M):
         assert torch.equal(fb.block_linear(*args), ref)
 
 
-def test_workspace_reused_across_calls():
-    """One zero-filled workspace serves consecutive split-K calls of different shapes."""
-    need = max(fb.workspace_size(M, N, K) for (M, N, K) in ((1, 9216, 7168), (8, 7168, 8192), (3, 384, 512)))
-    assert need > 0
-    wsp = torch.zeros(need, dtype=torch.uint8, device="cuda")
-    for i, (M, N, K) in enumerate(((1, 9216, 7168), (8, 7168, 8192), (3, 384, 512), (1, 9216, 7168))):
+def test_workspace_argument_is_accepted():
+    """A caller-provided workspace (the ABI's optional scratch) changes nothing."""
+    wsp = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
+    for i, (M, N, K) in enumerate(((1, 9216, 7168), (8, 7168, 8192), (3, 384, 512))):
         x, w = inputs(M, N, K, seed=40 + i)
-        check_linear(x, w, f"shared workspace call {i}", workspace=wsp)
+        a = check_linear(x, w, f"with workspace {i}", workspace=wsp)
+        b = gpu_path(x, w)
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("M,K", [(16, 12288), (9, 20480)])
+def test_decode_activations_beyond_lds(M, K):
+    """M x K codes too large to stage in LDS: B fragments are read from global memory."""
+    x, w = inputs(M, 256, K, seed=70 + M)
+    check_linear(x, w, "decode, activations from global")
+
+
+@pytest.mark.parametrize("waves", [1, 2, 3, 5, 7, 16])
+def test_decode_split_counts(waves, monkeypatch):
+    """Every split-K degree of the decode schedule meets the tolerance."""
+    monkeypatch.setenv("FP8BS_DECODE_WAVES", str(waves))
+    x, w = inputs(5, 384, 2048, seed=50 + waves)
+    check_linear(x, w, f"decode waves={waves}")
 
 
 def test_subnormal_codes_and_scales():
@@ -144,3 +159,29 @@ def test_subnormal_codes_and_scales():
     q, s = oracle.quant_act(x)
     assert np.any((q & 0x78) == 0) and np.any(s < np.finfo(np.float32).tiny)
     check_linear(x, w, "subnormal codes")
+
+
+def test_graph_replay_matches_eager():
+    """The path captured in a HIP graph (as the bench runs it) reproduces the eager
+    outputs on every replay, with eager work in between."""
+    x, w = inputs(8, 2048, 3072, seed=60)
+    xd, wd = dev_bf16(x), dev_bf16(w)
+    qw, ws = fb.quant_weight(wd)
+    q = torch.empty((8, 3072), dtype=torch.uint8, device="cuda")
+    s = torch.empty((8, 24), dtype=torch.float32, device="cuda")
+    y = torch.empty((8, 2048), dtype=torch.bfloat16, device="cuda")
+    fb.quant_act(xd, q, s)
+    fb.block_linear(q, s, qw, ws, out=y)
+    torch.cuda.synchronize()
+    ref_q, ref_s, ref_y = q.clone(), s.clone(), y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fb.quant_act(xd, q, s)
+        fb.block_linear(q, s, qw, ws, out=y)
+    for i in range(4):
+        q.zero_(); s.zero_(); y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(q, ref_q) and torch.equal(s, ref_s) and torch.equal(y, ref_y), i
+        fb.block_linear(q, s, qw, ws)          # eager work between replays
+        torch.cuda.synchronize()
