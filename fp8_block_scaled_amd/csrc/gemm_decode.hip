@@ -21,11 +21,11 @@
 //     time (32 VGPRs).  At ~60 VGPRs a CU holds 32 waves, so the workgroups of
 //     every decode shape (up to 1024 strips of up to 8 waves) are resident at once
 //     and no second, mostly idle round of workgroups is needed.
-//   * The M x K activation codes (at most a few tens of KB at decode) are staged
-//     in LDS by the whole workgroup with direct global -> LDS loads (no VGPRs)
-//     while the weight loads are in flight; each wave then reads its B fragments
-//     from LDS.  When M x K does not fit LDS the B fragments come straight from
-//     global memory (L2).
+//   * Each wave stages its own K slice of the M x K activation codes (at most a
+//     few tens of KB in all at decode) in LDS with direct global -> LDS loads (no
+//     VGPRs) while its weight loads are in flight, then reads its B fragments from
+//     LDS.  The waves never wait for each other until the final reduction.  When
+//     M x K does not fit LDS the B fragments come straight from global memory (L2).
 //   * Both scales of a K block are requested together with its weight fragments;
 //     the weight scale is a scalar load (the wave index is made wave-uniform).
 //
@@ -77,43 +77,57 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
     const float* xsrow = a.xs + (mvalid ? r : 0) * a.KB;
 
     // One chunk: the weight fragments and both scales of up to kChunk K blocks, all
-    // requested before any is used.
+    // requested before any is used.  The loads are branch-free (indices past the
+    // wave's range are clamped to its last K block and their results unused), so
+    // the compiler issues them back to back without intermediate waits.
     v4i wv[kChunk][2];
     float xsv[kChunk], wsv[kChunk];
-    auto load_chunk = [&](int64_t kb, int n) {
+    auto load_chunk = [&](int64_t kb) {
 #pragma unroll
         for (int i = 0; i < kChunk; ++i) {
-            if (i < n) {
-                const v4i* p = reinterpret_cast<const v4i*>(wrow + (kb + i) * kGroup);
-                wv[i][0] = p[0];
-                wv[i][1] = p[4];
-            }
+            const int64_t k = kb + i < kb1 ? kb + i : kb1 - 1;
+            const v4i* p = reinterpret_cast<const v4i*>(wrow + k * kGroup);
+            wv[i][0] = p[0];
+            wv[i][1] = p[4];
         }
 #pragma unroll
         for (int i = 0; i < kChunk; ++i) {
-            if (i < n) {
-                wsv[i] = wsrow[kb + i];
-                xsv[i] = mvalid ? xsrow[kb + i] : 0.0f;
-            }
+            const int64_t k = kb + i < kb1 ? kb + i : kb1 - 1;
+            wsv[i] = wsrow[k];
+            xsv[i] = xsrow[k];                       // used only by lanes with mvalid
         }
     };
+    // Wave-private staging of this wave's K slice of the activation codes: rows
+    // [0, M) x bytes [128 kb0, 128 kb1), stored row-major at LDS offset M * 128 kb0
+    // (the slices of the S waves tile the M x K codes).  Direct global -> LDS loads:
+    // lane l of an instruction writes LDS bytes [16 l, 16 l + 16) past its base, so
+    // one instruction moves 64 consecutive 16-byte pieces of the slice.  Only this
+    // wave reads its slice, so no barrier is needed: the wave's own vmcnt wait
+    // before the first fragment read covers it.
+    const int64_t slice_len = (kb1 - kb0) * kGroup;            // bytes per row
+    uint8_t* slice = xlds + (int64_t)a.M * kb0 * kGroup;
+    if (kXInLds) {
+        const int64_t per_row = slice_len / 16;
+        const int64_t pieces = (int64_t)a.M * per_row;
+        for (int64_t c0 = 0; c0 < pieces; c0 += 64) {
+            const int64_t c = c0 + lane;
+            if (c < pieces) {
+                const int64_t row = c / per_row, col = c - row * per_row;
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(a.x + row * a.K + kb0 * kGroup + col * 16),
+                    (__attribute__((address_space(3))) void*)(slice + c0 * 16), 16, 0, 0);
+            }
+        }
+    }
+
     int64_t kb = kb0;
     int n = (int)(kb1 - kb < kChunk ? kb1 - kb : kChunk);
-    load_chunk(kb, n);
-
+    if (n > 0) load_chunk(kb);
     if (kXInLds) {
-        // Stage the M x K activation codes, row-major and unpadded, with direct
-        // global -> LDS loads: lane l of a wave writes LDS bytes [16 l, 16 l + 16)
-        // past the wave's base, so a wave moves 64 consecutive 16-byte pieces.
-        const int64_t pieces = (int64_t)a.M * (a.K / 16);
-        for (int64_t c0 = (int64_t)wave * 64; c0 < pieces; c0 += (int64_t)S * 64) {
-            const int64_t c = c0 + lane;
-            if (c < pieces)
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.x + c * 16),
-                                                 (__attribute__((address_space(3))) void*)(xlds + c0 * 16), 16, 0, 0);
-        }
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the LDS writes of this wave have landed
-        __syncthreads();
+        // The compiler does not see the LDS side of global_load_lds: wait for it
+        // (and the first chunk) explicitly, with a memory clobber so that no LDS
+        // read is scheduled above.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -125,7 +139,7 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
                 const int64_t k = kb + i;
                 v4i b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
                 if (mvalid) {
-                    const uint8_t* xp = kXInLds ? xlds + r * a.K + k * kGroup + 16 * g
+                    const uint8_t* xp = kXInLds ? slice + r * slice_len + (k - kb0) * kGroup + 16 * g
                                                 : a.x + r * a.K + k * kGroup + 16 * g;
                     b0 = reinterpret_cast<const v4i*>(xp)[0];
                     b1 = reinterpret_cast<const v4i*>(xp)[4];
@@ -135,7 +149,7 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
                 const v8i bv = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
                 // Format 0 = E4M3 for both operands; zero scale operands select the unscaled MFMA.
                 const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, zero, 0, 0, 0, 0, 0, 0);
-                const float sc = xsv[i] * wsv[i];
+                const float sc = (mvalid ? xsv[i] : 0.0f) * wsv[i];
                 acc[0] = fmaf(sc, p[0], acc[0]);
                 acc[1] = fmaf(sc, p[1], acc[1]);
                 acc[2] = fmaf(sc, p[2], acc[2]);
@@ -144,7 +158,7 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
         }
         kb += n;
         n = (int)(kb1 - kb < kChunk ? kb1 - kb : kChunk);
-        if (n > 0) load_chunk(kb, n);
+        if (n > 0) load_chunk(kb);
     }
 
     __syncthreads();                        // every wave is done reading the staged codes
