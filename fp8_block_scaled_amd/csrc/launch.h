@@ -12,11 +12,14 @@ hipError_t launch_quant_act(const void* x, void* q, float* s, int64_t M, int64_t
 hipError_t launch_silu_mul_quant(const void* gu, void* q, float* s, int64_t M, int64_t I, hipStream_t st);
 hipError_t launch_quant_weight(const void* w, void* qw, float* ws, int64_t N, int64_t K, hipStream_t st);
 
-// ---- decode GEMM (M <= kDecodeMaxM): one workgroup per 16-column strip, split-K over its waves
+// ---- decode GEMM (M <= kDecodeMaxM): one workgroup per strip of `rows` columns, split-K over its waves
 constexpr int kDecodeMaxM = 16;
 
 struct DecodePlan {
-    int64_t strips;      // N / 16: workgroups
+    int rows;            // 4, 8 or 16: token rows per MFMA group = output columns per strip
+    int strips_per_wg;   // 1..4 adjacent strips per workgroup
+    int64_t strips;      // N / rows
+    int64_t workgroups;  // ceil(strips / strips_per_wg)
     int64_t kblocks;     // K / 128
     int waves;           // waves per workgroup = K splits
 };

@@ -140,6 +140,15 @@ def test_decode_activations_beyond_lds(M, K):
     check_linear(x, w, "decode, activations from global")
 
 
+@pytest.mark.parametrize("strips", [1, 2, 3, 4])
+@pytest.mark.parametrize("M,N", [(1, 640), (5, 384), (8, 1152), (12, 640)])
+def test_decode_strips_per_workgroup(strips, M, N, monkeypatch):
+    """Every strips-per-workgroup setting, including a partial last workgroup."""
+    monkeypatch.setenv("FP8BS_DECODE_STRIPS", str(strips))
+    x, w = inputs(M, N, 1408, seed=80 + strips + M)
+    check_linear(x, w, f"decode strips={strips}")
+
+
 @pytest.mark.parametrize("waves", [1, 2, 3, 5, 7, 16])
 def test_decode_split_counts(waves, monkeypatch):
     """Every split-K degree of the decode schedule meets the tolerance."""
