@@ -4,20 +4,28 @@
 // ("Nanbeige4.3-33B FP8" model card, introduction: E4M3 weights in 128x128 blocks,
 // dynamic per-token group-128 activation scales; FP32 accumulation, BF16 out).
 //
-// Tiling: a 256-thread workgroup computes a 128 (m) x 128 (n) output tile; each of
-// its 4 waves owns 64 x 64.  The K loop steps one 128-wide scale block at a time:
-//   1. the 128x128-byte tiles of q and w for the next K block are loaded from
-//      global memory into registers while the current block is computed;
-//   2. each wave issues 4 x 4 v_mfma_f32_16x16x128_f8f6f4 (A = 16 weight rows,
-//      B = 16 token rows; one MFMA covers the whole K block), and folds every
-//      16x16 FP32 result into its accumulators with acc += (s[m] * ws[nb]) * P:
-//      the promotion of partial sums per 128-wide K block;
-//   3. the prefetched tiles are written to the other LDS buffer.
-// LDS rows are 128 bytes; 16-byte chunk c of row r is stored at chunk position
-// c ^ ((r >> 1) & 7), so the 16 rows a fragment read touches map to 16 distinct
-// 4-bank groups.
-// The n-range of a wave lies inside one 128-row weight block, so every lane needs
-// one weight scale and 4 token scales per K block.
+// Tiling: a workgroup of 8 waves computes a BM (m) x BN (n) output tile, the waves
+// arranged 4 (m) x 2 (n), each owning (BM/4) x (BN/2).  The K loop steps one
+// 128-wide scale block at a time through two LDS stages:
+//   1. at the top of step kb the wave waits for its own copies into stage kb%2
+//      and the workgroup meets at a barrier; the copies of K block kb + 1 into the
+//      other stage are then issued -- direct global -> LDS loads
+//      (global_load_lds_dwordx4: no VGPRs, no LDS write instructions), overlapping
+//      the compute of step kb;
+//   2. each wave runs v_mfma_f32_16x16x128_f8f6f4 over its 16 x 16 subtiles (A = 16
+//      weight rows, B = 16 token rows; one MFMA covers the whole K block) and folds
+//      each FP32 result into its accumulators with acc += (s[m] * ws[nb]) * P: the
+//      promotion of partial sums per 128-wide K block.
+// LDS rows are 128 bytes; 16-byte chunk c of tile row r is stored at chunk
+// position c ^ ((r >> 1) & 7), so the 16 rows a fragment read touches fall in 16
+// distinct 4-bank groups.  A direct-to-LDS load writes lane l's 16 bytes at
+// position l of the wave's 1 KiB destination, so the swizzle is applied by
+// choosing which source chunk each lane fetches (8 lanes per 128-byte row: still
+// whole cache lines).
+// BN/2 <= 128 and tiles start at multiples of BN, so a wave's n-range lies in one
+// 128-row weight block: one weight scale per lane per K block, plus one token scale
+// per m-subtile.  Rows past M (the ragged last m-tile) load the last valid row and
+// are not stored.
 // Workgroup ids are remapped so that the tiles each XCD receives are contiguous in
 // a grouped (8 tile-rows) raster order: tiles that share q rows or w rows then
 // share an XCD's L2.
@@ -26,9 +34,8 @@
 
 namespace fp8bs {
 
-constexpr int kBM = 128, kBN = 128;
-constexpr int kPrefillThreads = 256;
-constexpr int kTileBytes = 128 * 128;
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillThreads = kPrefillWaves * 64;
 constexpr int kGroupRows = 8;
 constexpr int kXcds = 8;
 
@@ -50,15 +57,22 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int g) {
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
-__global__ __launch_bounds__(kPrefillThreads, 2) void gemm_prefill_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileBytes];   // [stage][w, x]
+template <int BM, int BN>
+__global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(PrefillArgs a) {
+    constexpr int WTM = BM / 4, WTN = BN / 2;          // wave tile (m, n)
+    constexpr int TJ = WTM / 16, TI = WTN / 16;         // subtiles (m, n)
+    constexpr int kStage = (BM + BN) * 128;             // bytes per LDS stage
+    constexpr int kCopies = (BM + BN) * 8 / kPrefillThreads;   // 16-byte copies per thread per stage
+    static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's n-range must lie in one weight block");
+    static_assert((BM + BN) * 8 % kPrefillThreads == 0, "copies must divide evenly");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     // ---- tile selection: XCD-contiguous, grouped raster
     const int64_t T = a.tiles_m * a.tiles_n;
     const int64_t b = blockIdx.x;
-    const int64_t xcd = b % kXcds, j = b / kXcds;
+    const int64_t xcd = b % kXcds, jx = b / kXcds;
     const int64_t per = T / kXcds, extra = T % kXcds;
-    const int64_t t = xcd * per + (xcd < extra ? xcd : extra) + j;
+    const int64_t t = xcd * per + (xcd < extra ? xcd : extra) + jx;
     const int64_t group_span = kGroupRows * a.tiles_n;
     const int64_t grp = t / group_span;
     const int64_t first_m = grp * kGroupRows;
@@ -66,122 +80,145 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void gemm_prefill_kernel(Prefil
     const int64_t in_grp = t - grp * group_span;
     const int64_t tm = first_m + in_grp % gm;
     const int64_t tn = in_grp / gm;
-    const int64_t m0 = tm * kBM, n0 = tn * kBN;
+    const int64_t m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wn = wave & 1, wm = wave >> 1;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
     const int g = lane >> 4, r = lane & 15;
 
-    // ---- global -> register assignment: chunk id tid + 256 i, 8 chunks per row
-    const uint8_t* wsrc[4];
-    const uint8_t* xsrc[4];
-    bool xok[4];
-    int ldst[4];
+    // ---- copy assignment: stage rows [0, BN) are w rows n0.., rows [BN, BN+BM) are
+    // q rows m0..; copy i of this wave moves 8 rows (64 chunks) starting at row
+    // 8 (wave * kCopies + i); lane l takes row + l / 8, LDS chunk position l % 8,
+    // i.e. source chunk (l % 8) ^ ((row >> 1) & 7).  Whether a copy reads w or q is
+    // wave-uniform (BN is a multiple of 8), so each copy is a scalar base plus a
+    // 32-bit per-lane offset (operands are below 4 GiB).
+    uint32_t src_off[kCopies];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int cid = tid + 256 * i;
-        const int row = cid >> 3, c = cid & 7;
-        wsrc[i] = a.w + (n0 + row) * a.K + c * 16;
-        xok[i] = (m0 + row) < a.M;
-        xsrc[i] = a.x + (xok[i] ? (m0 + row) : 0) * a.K + c * 16;
-        ldst[i] = swz(row, c);
+    for (int i = 0; i < kCopies; ++i) {
+        const int row = 8 * (wave * kCopies + i) + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+        if (8 * (wave * kCopies + i) < BN) {
+            src_off[i] = (uint32_t)((n0 + row) * a.K + chunk * 16);
+        } else {
+            int64_t mr = m0 + (row - BN);
+            mr = mr < a.M ? mr : a.M - 1;
+            src_off[i] = (uint32_t)(mr * a.K + chunk * 16);
+        }
     }
-    v4i wreg[4], xreg[4];
-    auto gload = [&](int64_t kb) {
+    auto copy_stage = [&](int64_t kb, int stage) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wreg[i] = *reinterpret_cast<const v4i*>(wsrc[i] + kb * kGroup);
-            xreg[i] = xok[i] ? *reinterpret_cast<const v4i*>(xsrc[i] + kb * kGroup) : v4i{0, 0, 0, 0};
+        for (int i = 0; i < kCopies; ++i) {
+            const uint8_t* base = (8 * (wave * kCopies + i) < BN ? a.w : a.x) + kb * kGroup;
+            uint8_t* dst = lds + stage * kStage + (wave * kCopies + i) * 1024;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + src_off[i]),
+                                             (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         }
     };
-    auto lstore = [&](int stage) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<v4i*>(&lds[stage][0][ldst[i]]) = wreg[i];
-            *reinterpret_cast<v4i*>(&lds[stage][1][ldst[i]]) = xreg[i];
-        }
-    };
 
-    // ---- scales: token rows of this lane's 4 B fragments, and the weight block row
-    const float* xs_row[4];
-    bool mok[4];
+    // ---- scales: token rows of this lane's TJ B fragments, and the weight block row
+    uint32_t xs_off[TJ];
+    bool mok[TJ];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        const int64_t m = m0 + wm * 64 + 16 * jj + r;
-        mok[jj] = m < a.M;
-        xs_row[jj] = a.xs + (mok[jj] ? m : 0) * a.KB;
+    for (int j = 0; j < TJ; ++j) {
+        const int64_t m = m0 + wm * WTM + 16 * j + r;
+        mok[j] = m < a.M;
+        xs_off[j] = (uint32_t)((mok[j] ? m : a.M - 1) * a.KB);
     }
-    const float* ws_row = a.ws + (n0 / kGroup) * a.KB;
-    float xsc[4], wsc;
-    float xsc_n[4], wsc_n;
-    auto sload = [&](int64_t kb, float (&xs_)[4], float& ws_) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) xs_[jj] = mok[jj] ? xs_row[jj][kb] : 0.0f;
-        ws_ = ws_row[kb];
-    };
+    const float* ws_row = a.ws + ((n0 + wn * WTN) / kGroup) * a.KB;
+    float xsc[TJ], wsc, xsn[TJ], wsn;
 
-    v4f acc[4][4];
+    v4f acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    gload(0);
-    sload(0, xsc, wsc);
-    lstore(0);
+    copy_stage(0, 0);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) xsn[j] = a.xs[xs_off[j]];
+    wsn = ws_row[0];
 
     for (int64_t kb = 0; kb < a.KB; ++kb) {
-        __syncthreads();
         const int stage = (int)(kb & 1);
-        const bool more = kb + 1 < a.KB;
-        if (more) {
-            gload(kb + 1);
-            sload(kb + 1, xsc_n, wsc_n);
+        // This wave's copies into `stage` (and the scale loads) have landed; the
+        // barrier makes everyone's visible and frees the other stage.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) xsc[j] = xsn[j];
+        wsc = wsn;
+        if (kb + 1 < a.KB) {
+            copy_stage(kb + 1, stage ^ 1);
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) xsn[j] = a.xs[xs_off[j] + kb + 1];
+            wsn = ws_row[kb + 1];
         }
-        const uint8_t* wt = lds[stage][0];
-        const uint8_t* xt = lds[stage][1];
-        v8i bf[4];
+        const uint8_t* wt = lds + stage * kStage;
+        const uint8_t* xt = wt + BN * 128;
+        v8i bf[TJ];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) bf[jj] = lds_frag(xt, wm * 64 + 16 * jj + r, g);
-        float sc[4];
+        for (int j = 0; j < TJ; ++j) bf[j] = lds_frag(xt, wm * WTM + 16 * j + r, g);
+        float sc[TJ];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sc[jj] = xsc[jj] * wsc;
+        for (int j = 0; j < TJ; ++j) sc[j] = xsc[j] * wsc;
+        // Subtile row i: TJ independent MFMAs (own result registers), then their
+        // promotions; the next A fragment is read from LDS meanwhile.
+        v8i af_next = lds_frag(wt, wn * WTN + r, g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const v8i af = lds_frag(wt, wn * 64 + 16 * i + r, g);
+        for (int i = 0; i < TI; ++i) {
+            const v8i af = af_next;
+            if (i + 1 < TI) af_next = lds_frag(wt, wn * WTN + 16 * (i + 1) + r, g);
+            v4f p[TJ];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
+            for (int j = 0; j < TJ; ++j) {
                 const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[jj], zero, 0, 0, 0, 0, 0, 0);
-                acc[i][jj][0] = fmaf(sc[jj], p[0], acc[i][jj][0]);
-                acc[i][jj][1] = fmaf(sc[jj], p[1], acc[i][jj][1]);
-                acc[i][jj][2] = fmaf(sc[jj], p[2], acc[i][jj][2]);
-                acc[i][jj][3] = fmaf(sc[jj], p[3], acc[i][jj][3]);
+                // Format 0 = E4M3 for both operands; zero scale operands select the unscaled MFMA.
+                p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], zero, 0, 0, 0, 0, 0, 0);
             }
-        }
-        if (more) {
-            lstore(stage ^ 1);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) xsc[jj] = xsc_n[jj];
-            wsc = wsc_n;
+            for (int j = 0; j < TJ; ++j) {
+                acc[i][j][0] = fmaf(sc[j], p[j][0], acc[i][j][0]);
+                acc[i][j][1] = fmaf(sc[j], p[j][1], acc[i][j][1]);
+                acc[i][j][2] = fmaf(sc[j], p[j][2], acc[i][j][2]);
+                acc[i][j][3] = fmaf(sc[j], p[j][3], acc[i][j][3]);
+            }
         }
     }
 
-    // ---- epilogue: lane holds y[m][n .. n + 3] for each (i, jj)
+    // ---- epilogue: lane holds y[m][n .. n + 3] for each (i, j)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        if (!mok[jj]) continue;
-        const int64_t m = m0 + wm * 64 + 16 * jj + r;
+    for (int j = 0; j < TJ; ++j) {
+        if (!mok[j]) continue;
+        const int64_t m = m0 + wm * WTM + 16 * j + r;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t n = n0 + wn * 64 + 16 * i + 4 * g;
+        for (int i = 0; i < TI; ++i) {
+            const int64_t n = n0 + wn * WTN + 16 * i + 4 * g;
             uint2 o;
-            o.x = f32_to_bf16_rne(acc[i][jj][0]) | (f32_to_bf16_rne(acc[i][jj][1]) << 16);
-            o.y = f32_to_bf16_rne(acc[i][jj][2]) | (f32_to_bf16_rne(acc[i][jj][3]) << 16);
+            o.x = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
+            o.y = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
             *reinterpret_cast<uint2*>(a.y + m * a.N + n) = o;
         }
     }
+}
+
+template <int BM, int BN>
+static hipError_t launch_tiles(PrefillArgs a, hipStream_t st) {
+    a.tiles_m = (a.M + BM - 1) / BM;
+    a.tiles_n = a.N / BN;
+    const int64_t T = a.tiles_m * a.tiles_n;
+    if (T == 0) return hipSuccess;
+    constexpr int lds = 2 * (BM + BN) * 128;
+    static bool attr_set = false;          // idempotent; a race only repeats the call
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_prefill_kernel<BM, BN>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((gemm_prefill_kernel<BM, BN>), dim3((unsigned)T), dim3(kPrefillThreads), lds, st, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, const float* ws, void* y,
@@ -197,12 +234,8 @@ hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, con
     a.N = N;
     a.K = K;
     a.KB = K / kGroup;
-    a.tiles_m = (M + kBM - 1) / kBM;
-    a.tiles_n = N / kBN;
-    const int64_t T = a.tiles_m * a.tiles_n;
-    if (T == 0) return hipSuccess;
-    hipLaunchKernelGGL(gemm_prefill_kernel, dim3((unsigned)T), dim3(kPrefillThreads), 0, st, a);
-    return hipGetLastError();
+    if (N % 256 == 0) return launch_tiles<256, 256>(a, st);
+    return launch_tiles<256, 128>(a, st);
 }
 
 }  // namespace fp8bs
