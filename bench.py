@@ -56,6 +56,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true", help="skip the other workloads")
     p.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    p.add_argument("--summarize", metavar="DIR",
+                   help="print a per-kernel summary of the rocprofv3 CSV output under DIR and exit")
     return p.parse_args()
 
 
@@ -209,8 +211,40 @@ def cpu_baseline(wl, budget_s=12.0):
                        f"{el:.1f} s, {per_step * 1e3:.1f} ms/step")}
 
 
+def summarize_rocprof(directory):
+    """Per-kernel, per-grid summary of rocprofv3 CSV output (kernel trace and/or
+    counter collection) found under ``directory``: dispatch count, mean and min
+    duration, and the mean of every collected counter."""
+    import csv
+    import glob
+    from collections import defaultdict
+    rows_t = defaultdict(list)
+    rows_c = defaultdict(lambda: defaultdict(list))
+    for f in glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                key = (r["Kernel_Name"], r.get("Grid_Size_X", r.get("Grid_Size", "")))
+                rows_t[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                key = (r["Kernel_Name"], r.get("Grid_Size", ""))
+                rows_c[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    for key in sorted(set(rows_t) | set(rows_c)):
+        name, grid = key
+        print(f"kernel {name}  grid {grid}")
+        if key in rows_t:
+            d = rows_t[key]
+            print(f"  dispatches {len(d)}  mean {sum(d) / len(d) / 1e3:.2f} us  min {min(d) / 1e3:.2f} us")
+        for cname, vals in sorted(rows_c.get(key, {}).items()):
+            print(f"  {cname} mean {sum(vals) / len(vals):.6g} over {len(vals)} dispatches")
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize_rocprof(args.summarize)
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)

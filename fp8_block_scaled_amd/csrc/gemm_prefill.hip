@@ -11,7 +11,11 @@
 //      and the workgroup meets at a barrier; the copies of K block kb + 1 into the
 //      other stage are then issued -- direct global -> LDS loads
 //      (global_load_lds_dwordx4: no VGPRs, no LDS write instructions), overlapping
-//      the compute of step kb;
+//      the compute of step kb.  Each thread also touches one 128-byte line of K
+//      block kb + 2 (a 4-byte direct-to-LDS load into a dump area) so that the
+//      copies of the next step find their lines in L2: a double-buffered 256 x 256
+//      tile fills 128 KB of LDS, leaving no room for a third stage, and the first
+//      touch of a line from HBM takes longer than one step of compute;
 //   2. each wave runs v_mfma_f32_16x16x128_f8f6f4 over its 16 x 16 subtiles (A = 16
 //      weight rows, B = 16 token rows; one MFMA covers the whole K block) and folds
 //      each FP32 result into its accumulators with acc += (s[m] * ws[nb]) * P: the
@@ -49,6 +53,12 @@ struct PrefillArgs {
     int64_t tiles_m, tiles_n;
 };
 
+// Bytes of one LDS stage: w tile, q tile, BM token scales, weight scales (one
+// wave's 4-byte copy writes 256 bytes; the first BN/128 are the tile's weight blocks).
+constexpr int stage_bytes(int BM, int BN) { return (BM + BN) * 128 + BM * 4 + 256; }
+// Dynamic LDS of a launch: two stages and the 256-byte warm-up dump.
+constexpr int prefill_lds_bytes(int BM, int BN) { return 2 * stage_bytes(BM, BN) + 256; }
+
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int g) {
@@ -61,7 +71,7 @@ template <int BM, int BN>
 __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(PrefillArgs a) {
     constexpr int WTM = BM / 4, WTN = BN / 2;          // wave tile (m, n)
     constexpr int TJ = WTM / 16, TI = WTN / 16;         // subtiles (m, n)
-    constexpr int kStage = (BM + BN) * 128;             // bytes per LDS stage
+    constexpr int kStage = stage_bytes(BM, BN);
     constexpr int kCopies = (BM + BN) * 8 / kPrefillThreads;   // 16-byte copies per thread per stage
     static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's n-range must lie in one weight block");
     static_assert((BM + BN) * 8 % kPrefillThreads == 0, "copies must divide evenly");
@@ -117,17 +127,56 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
         }
     };
 
-    // ---- scales: token rows of this lane's TJ B fragments, and the weight block row
-    uint32_t xs_off[TJ];
+    // ---- L2 warm-up of K block kb + 2: thread t touches stage row t mod (BM + BN)
+    // (one line).  Every thread issues it, so it is always each wave's last load.
+    static_assert(BM + BN <= kPrefillThreads, "one warm-up line per thread covers the stage");
+    const int pf_row = tid % (BM + BN);
+    const bool pf_w = pf_row < BN;
+    uint32_t pf_off;
+    {
+        int64_t row = pf_w ? n0 + pf_row : m0 + (pf_row - BN);
+        if (!pf_w) row = row < a.M ? row : a.M - 1;
+        pf_off = (uint32_t)(row * a.K);
+    }
+    auto warm = [&](int64_t kb) {
+        const uint8_t* base = (pf_w ? a.w : a.x) + kb * kGroup;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + pf_off),
+                                         (__attribute__((address_space(3))) void*)(lds + 2 * kStage), 4, 0, 0);
+    };
+
+    // ---- scales: the BM token scales and the weight-block scales of K block kb are
+    // copied into the stage with the tiles (4-byte direct-to-LDS loads), so the
+    // warm-up touch is always each wave's last vector load and nothing waits on it.
+    static_assert(BM % 64 == 0 && BM / 64 <= kPrefillWaves, "one scale copy per wave");
+    const bool xs_copy = wave < BM / 64;
+    uint32_t xs_off;
+    {
+        int64_t m = m0 + wave * 64 + lane;
+        m = m < a.M ? m : a.M - 1;
+        xs_off = (uint32_t)(m * a.KB);
+    }
+    auto copy_scales = [&](int64_t kb, int stage) {
+        if (xs_copy)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.xs + xs_off + kb),
+                                             (__attribute__((address_space(3))) void*)(lds + stage * kStage +
+                                                                                      (BM + BN) * 128 + wave * 256),
+                                             4, 0, 0);
+    };
+    // Weight scales of the tile's BN/128 weight blocks: wave BM/64 copies them (lane l
+    // takes block l mod (BN/128)).
+    static_assert(BM / 64 < kPrefillWaves, "a wave is left for the weight scales");
+    const bool ws_copy = wave == BM / 64;
+    const uint32_t ws_off = (uint32_t)((n0 / kGroup + lane % (BN / kGroup)) * a.KB);
+    auto copy_wscales = [&](int64_t kb, int stage) {
+        if (ws_copy)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.ws + ws_off + kb),
+                                             (__attribute__((address_space(3))) void*)(lds + stage * kStage +
+                                                                                      (BM + BN) * 128 + BM * 4),
+                                             4, 0, 0);
+    };
     bool mok[TJ];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-        const int64_t m = m0 + wm * WTM + 16 * j + r;
-        mok[j] = m < a.M;
-        xs_off[j] = (uint32_t)((mok[j] ? m : a.M - 1) * a.KB);
-    }
-    const float* ws_row = a.ws + ((n0 + wn * WTN) / kGroup) * a.KB;
-    float xsc[TJ], wsc, xsn[TJ], wsn;
+    for (int j = 0; j < TJ; ++j) mok[j] = m0 + wm * WTM + 16 * j + r < a.M;
 
     v4f acc[TI][TJ];
 #pragma unroll
@@ -136,33 +185,39 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
         for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     copy_stage(0, 0);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) xsn[j] = a.xs[xs_off[j]];
-    wsn = ws_row[0];
+    copy_scales(0, 0);
+    copy_wscales(0, 0);
+    warm(a.KB > 1 ? 1 : 0);
 
     for (int64_t kb = 0; kb < a.KB; ++kb) {
         const int stage = (int)(kb & 1);
-        // This wave's copies into `stage` (and the scale loads) have landed; the
-        // barrier makes everyone's visible and frees the other stage.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) xsc[j] = xsn[j];
-        wsc = wsn;
+        // This wave's copies into `stage` (and the scale loads) have landed -- all
+        // but the last load issued, the warm-up touch; the barrier makes everyone's
+        // copies visible and frees the other stage.
+        // A plain s_barrier: __syncthreads() would add a full vmcnt(0) wait (its
+        // fence) and so wait for the warm-up touch as well.  Every LDS read of the
+        // previous step was consumed before a wave reaches the barrier, and each
+        // wave has waited for its own copies above; the empty asm statements keep
+        // the compiler from moving LDS accesses across the barrier.
+        asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         if (kb + 1 < a.KB) {
             copy_stage(kb + 1, stage ^ 1);
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) xsn[j] = a.xs[xs_off[j] + kb + 1];
-            wsn = ws_row[kb + 1];
+            copy_scales(kb + 1, stage ^ 1);
+            copy_wscales(kb + 1, stage ^ 1);
         }
+        warm(kb + 2 < a.KB ? kb + 2 : a.KB - 1);       // always one warm-up load last
         const uint8_t* wt = lds + stage * kStage;
         const uint8_t* xt = wt + BN * 128;
         v8i bf[TJ];
 #pragma unroll
         for (int j = 0; j < TJ; ++j) bf[j] = lds_frag(xt, wm * WTM + 16 * j + r, g);
+        const float* xs_lds = reinterpret_cast<const float*>(xt + BM * 128);
+        const float wsc = reinterpret_cast<const float*>(xt + BM * 128 + BM * 4)[(wn * WTN) / kGroup];
         float sc[TJ];
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) sc[j] = xsc[j] * wsc;
+        for (int j = 0; j < TJ; ++j) sc[j] = xs_lds[wm * WTM + 16 * j + r] * wsc;
         // Subtile row i: TJ independent MFMAs (own result registers), then their
         // promotions; the next A fragment is read from LDS meanwhile.
         v8i af_next = lds_frag(wt, wn * WTN + r, g);
@@ -209,7 +264,7 @@ static hipError_t launch_tiles(PrefillArgs a, hipStream_t st) {
     a.tiles_n = a.N / BN;
     const int64_t T = a.tiles_m * a.tiles_n;
     if (T == 0) return hipSuccess;
-    constexpr int lds = 2 * (BM + BN) * 128;
+    constexpr int lds = prefill_lds_bytes(BM, BN);
     static bool attr_set = false;          // idempotent; a race only repeats the call
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)gemm_prefill_kernel<BM, BN>,
