@@ -56,6 +56,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true", help="skip the other workloads")
     p.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain 512 MiB device copy, 10 times (reference for HBM byte counters)")
     p.add_argument("--summarize", metavar="DIR",
                    help="print a per-kernel summary of the rocprofv3 CSV output under DIR and exit")
     return p.parse_args()
@@ -244,6 +246,15 @@ def main():
     args = parse()
     if args.summarize:
         summarize_rocprof(args.summarize)
+        return 0
+    if args.copy_calibration:
+        import torch
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 512 << 20, "copy_bytes_written": 512 << 20, "copies": 10}))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

@@ -33,6 +33,8 @@
 // Workgroup ids are remapped so that the tiles each XCD receives are contiguous in
 // a grouped (8 tile-rows) raster order: tiles that share q rows or w rows then
 // share an XCD's L2.
+#include <cstdlib>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -242,6 +244,10 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
         }
     }
 
+    // No direct-to-LDS load (the last warm-up touch) may still be in flight when
+    // the workgroup's LDS is released.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
     // ---- epilogue: lane holds y[m][n .. n + 3] for each (i, j)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
@@ -289,7 +295,10 @@ hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, con
     a.N = N;
     a.K = K;
     a.KB = K / kGroup;
-    if (N % 256 == 0) return launch_tiles<256, 256>(a, st);
+    bool wide = N % 256 == 0;
+    if (const char* e = getenv("FP8BS_PREFILL_TILE_N"))     // tuning hook: 128 or 256
+        wide = wide && atoi(e) != 128;
+    if (wide) return launch_tiles<256, 256>(a, st);
     return launch_tiles<256, 128>(a, st);
 }
 
