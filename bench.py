@@ -36,12 +36,22 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 MALL_BYTES = 256 << 20         # Infinity Cache
 METRIC = "FP8 block-GEMM TFLOP/s (prefill) and GB/s (decode M=1..8), % of roofline"
-KERNEL_SOURCES = ["gemm_decode.hip", "gemm_prefill.hip", "quant.hip", "device_common.h", "api.hip"]
+# Sources each GEMM kernel's HBM traffic depends on: a committed counter reading is
+# used only while these files are unchanged.
+KERNEL_SOURCES = {
+    "decode": ["gemm_decode.hip", "launch.h", "device_common.h", "api.hip"],
+    "prefill": ["gemm_prefill.hip", "launch.h", "device_common.h", "api.hip"],
+}
+DECODE_MAX_M = 16               # block_linear takes the decode kernel for M <= 16
 
 
-def kernel_source_hash():
+def gemm_kind(M):
+    return "decode" if M <= DECODE_MAX_M else "prefill"
+
+
+def kernel_source_hash(kind):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "fp8_block_scaled_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -56,6 +66,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true", help="skip the other workloads")
     p.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    p.add_argument("--make-traffic", metavar="DIR",
+                   help="write --traffic-file from rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR "
+                        "(DIR/<workload>/{fetch,write}, DIR/copy/{fetch,write})")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 512 MiB device copy, 10 times (reference for HBM byte counters)")
     p.add_argument("--summarize", metavar="DIR",
@@ -110,6 +123,21 @@ class Case:
         import fp8_block_scaled_amd as fb
         c = i % self.copies
         fb.block_linear(self.q, self.s, self.qw[c], self.ws[c], out=self.y, workspace=self.workspace)
+
+
+# Standard deviation of the gate/up output for x ~ N(0,1), W ~ N(0, 0.02^2), K = 7168.
+GU_SIGMA = 1.7
+
+
+def make_case(wl):
+    """A Case for workload ``wl``; the down projection takes SiLU(gate)*up of a seeded
+    gate/up tensor of the gate/up workload's output shape."""
+    import synth
+    from synth import WORKLOADS
+    if wl.x_kind == "silu":
+        gw = WORKLOADS["spec_mlp_gu"]
+        return Case(wl, gu_bits=synth.bf16_normal(gw.M, gw.N, GU_SIGMA, gw.seed, synth.TID_GU))
+    return Case(wl)
 
 
 def _replay_ms(graph):
@@ -168,7 +196,7 @@ def roofline_for(wl, gemm_us, traffic):
     return r
 
 
-def load_traffic(path, workload):
+def load_traffic(path, wl):
     """HBM bytes per GEMM dispatch from committed rocprofv3 counter runs, or None when
     absent or taken on different kernel sources."""
     try:
@@ -176,10 +204,64 @@ def load_traffic(path, workload):
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    ent = t.get("workloads", {}).get(wl.name)
+    if not ent or ent.get("kernel_source_hash") != kernel_source_hash(gemm_kind(wl.M)):
         return None
-    ent = t.get("workloads", {}).get(workload)
-    return ent.get("bytes_per_dispatch") if ent else None
+    return ent.get("bytes_per_dispatch")
+
+
+def _counter_means(directory, name_filter):
+    """{(kernel name, grid): {counter: mean value}} over rocprofv3 counter CSVs."""
+    import csv
+    import glob
+    from collections import defaultdict
+    acc = defaultdict(lambda: defaultdict(list))
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if name_filter in r["Kernel_Name"]:
+                    acc[(r["Kernel_Name"], r["Grid_Size"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in acc.items()}
+
+
+def make_traffic(directory, out_path):
+    """HBM bytes per GEMM dispatch = FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled by what that counter reads for a plain device copy of known size."""
+    from synth import WORKLOADS
+
+    def one(d, what, counter):
+        m = _counter_means(d, what)
+        if len(m) != 1:
+            raise SystemExit(f"{d}: expected one {what!r} kernel/grid, found {sorted(m)}")
+        (key, vals), = m.items()
+        return key, vals[counter]
+
+    copy_bytes = 512 << 20
+    _, copy_fetch = one(os.path.join(directory, "copy", "fetch"), "copyBuffer", "FETCH_SIZE")
+    _, copy_write = one(os.path.join(directory, "copy", "write"), "copyBuffer", "WRITE_SIZE")
+    f_fac, w_fac = copy_bytes / (copy_fetch * 1024), copy_bytes / (copy_write * 1024)
+    doc = {"method": ("rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, on bench.py --workload W "
+                      "--no-others, kernels matching gemm_; KiB per dispatch x 1024 x the factor that "
+                      "maps the same counter onto a 512 MiB device copy's bytes"),
+           "copy_factor": {"FETCH_SIZE": round(f_fac, 4), "WRITE_SIZE": round(w_fac, 4)},
+           "workloads": {}}
+    for name, wl in WORKLOADS.items():
+        d = os.path.join(directory, name)
+        if not os.path.isdir(d):
+            continue
+        kf, fetch = one(os.path.join(d, "fetch"), "gemm_", "FETCH_SIZE")
+        kw, write = one(os.path.join(d, "write"), "gemm_", "WRITE_SIZE")
+        assert kf == kw, (kf, kw)
+        total = fetch * 1024 * f_fac + write * 1024 * w_fac
+        doc["workloads"][name] = {
+            "kernel": kf[0], "grid": int(kf[1]), "kernel_source_hash": kernel_source_hash(gemm_kind(wl.M)),
+            "fetch_kib": round(fetch, 1), "write_kib": round(write, 1),
+            "bytes_per_dispatch": int(round(total)), "algorithmic_bytes": wl.gemm_bytes(),
+            "ratio_to_algorithmic": round(total / wl.gemm_bytes(), 3)}
+    with open(out_path, "w") as fh:
+        json.dump(doc, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(doc, indent=1))
 
 
 def cpu_baseline(wl, budget_s=12.0):
@@ -247,6 +329,9 @@ def main():
     if args.summarize:
         summarize_rocprof(args.summarize)
         return 0
+    if args.make_traffic:
+        make_traffic(args.make_traffic, args.traffic_file)
+        return 0
     if args.copy_calibration:
         import torch
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -271,11 +356,11 @@ def main():
     torch.cuda.set_device(0)
     wl = WORKLOADS[args.workload]
     print(f"[bench] {wl.name}: setup", file=sys.stderr, flush=True)
-    case = Case(wl)
+    case = make_case(wl)
     ms, gemm_us, quant_us = time_case(case, args.steps, args.warmup)
     step_bytes = wl.quant_bytes() + wl.gemm_bytes()
     value = step_bytes / (ms * 1e-3) / 1e9
-    traffic = load_traffic(args.traffic_file, wl.name)
+    traffic = load_traffic(args.traffic_file, wl)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -306,14 +391,10 @@ def main():
                 continue
             w2 = WORKLOADS[name]
             print(f"[bench] {name}: setup", file=sys.stderr, flush=True)
-            if name == "spec_mlp_down":
-                gu = synth.bf16_normal(8, 16384, 1.7, w2.seed, synth.TID_GU)
-                c2 = Case(w2, gu_bits=gu)
-            else:
-                c2 = Case(w2)
+            c2 = make_case(w2)
             steps = max(5, min(args.steps, 50 if w2.M > 16 else args.steps))
             ms2, g2, q2 = time_case(c2, steps, max(2, min(args.warmup, 5)))
-            rl = roofline_for(w2, g2, load_traffic(args.traffic_file, name))
+            rl = roofline_for(w2, g2, load_traffic(args.traffic_file, w2))
             others[name] = {"M": w2.M, "K": w2.K, "N": w2.N, "ms_per_step": round(ms2, 5),
                             "block_linear_us": round(g2, 2), "quant_us": round(q2, 2),
                             "gemm_roofline": rl, "weight_copies_rotated": c2.copies}
