@@ -9,13 +9,14 @@
 // 128-wide scale block at a time through two LDS stages:
 //   1. at the top of step kb the wave waits for its own copies into stage kb%2
 //      and the workgroup meets at a barrier; the copies of K block kb + 1 into the
-//      other stage are then issued -- direct global -> LDS loads
-//      (global_load_lds_dwordx4: no VGPRs, no LDS write instructions), overlapping
-//      the compute of step kb.  Each thread also touches one 128-byte line of K
-//      block kb + 2 (a 4-byte direct-to-LDS load into a dump area) so that the
-//      copies of the next step find their lines in L2: a double-buffered 256 x 256
-//      tile fills 128 KB of LDS, leaving no room for a third stage, and the first
-//      touch of a line from HBM takes longer than one step of compute;
+//      other stage are then issued, two per subtile row over the first rows --
+//      direct global -> LDS loads (global_load_lds_dwordx4: no VGPRs, no LDS write
+//      instructions), overlapping the compute of step kb.  Each thread also
+//      touches one 128-byte line of K block kb + 2 (a 4-byte direct-to-LDS load
+//      into a dump area) so that the copies of the next step find their lines in
+//      L2: a double-buffered 256 x 256 tile fills 128 KB of LDS, leaving no room
+//      for a third stage, and the first touch of a line from HBM takes longer
+//      than one step of compute;
 //   2. each wave runs v_mfma_f32_16x16x128_f8f6f4 over its 16 x 16 subtiles (A = 16
 //      weight rows, B = 16 token rows; one MFMA covers the whole K block) and folds
 //      each FP32 result into its accumulators with acc += (s[m] * ws[nb]) * P: the
@@ -69,7 +70,7 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int g) {
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
-template <int BM, int BN>
+template <int BM, int BN, bool CLAMP>
 __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(PrefillArgs a) {
     constexpr int WTM = BM / 4, WTN = BN / 2;          // wave tile (m, n)
     constexpr int TJ = WTM / 16, TI = WTN / 16;         // subtiles (m, n)
@@ -77,6 +78,8 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
     constexpr int kCopies = (BM + BN) * 8 / kPrefillThreads;   // 16-byte copies per thread per stage
     static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's n-range must lie in one weight block");
     static_assert((BM + BN) * 8 % kPrefillThreads == 0, "copies must divide evenly");
+    static_assert(kCopies % 2 == 0 && BN % 8 == 0, "copies: 8-row groups, an even count per wave");
+    static_assert(kCopies / 2 <= TI, "two copies per subtile row");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     // ---- tile selection: XCD-contiguous, grouped raster
@@ -92,7 +95,11 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
     const int64_t in_grp = t - grp * group_span;
     const int64_t tm = first_m + in_grp % gm;
     const int64_t tn = in_grp / gm;
-    const int64_t m0 = tm * BM, n0 = tn * BN;
+    // Without CLAMP (M >= BM) the last tile row is moved back to end at row M - 1:
+    // every row it loads is valid, and the rows it shares with the tile row before
+    // are computed identically by both and stored twice with the same value.
+    const int64_t m0 = CLAMP ? tm * BM : (tm * BM + BM <= a.M ? tm * BM : a.M - BM);
+    const int64_t n0 = tn * BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -101,32 +108,53 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
     const int g = lane >> 4, r = lane & 15;
 
     // ---- copy assignment: stage rows [0, BN) are w rows n0.., rows [BN, BN+BM) are
-    // q rows m0..; copy i of this wave moves 8 rows (64 chunks) starting at row
-    // 8 (wave * kCopies + i); lane l takes row + l / 8, LDS chunk position l % 8,
-    // i.e. source chunk (l % 8) ^ ((row >> 1) & 7).  Whether a copy reads w or q is
-    // wave-uniform (BN is a multiple of 8), so each copy is a scalar base plus a
-    // 32-bit per-lane offset (operands are below 4 GiB).
-    uint32_t src_off[kCopies];
+    // q rows m0..; copy c of this wave moves the 8 tile rows starting at
+    // R = 8 (wave * kCopies + c) (64 chunks, 1 KiB of LDS); lane l takes row R + l / 8
+    // and LDS chunk position l % 8, i.e. source chunk (l % 8) ^ ((row >> 1) & 7).
+    // An 8-row group lies in one operand (BN is a multiple of 8), so each copy is a
+    // wave-uniform base (row R's address) plus a 32-bit lane offset.  The lane
+    // offset depends on c only through the parity of R / 8 (the swizzle), which is
+    // the parity of c (kCopies is even): two offsets serve all copies -- except
+    // with CLAMP, where rows past M are replaced by row M - 1 and the offset is
+    // formed per copy.
+    const int lrow = lane >> 3;
+    uint32_t voff[2];
 #pragma unroll
-    for (int i = 0; i < kCopies; ++i) {
-        const int row = 8 * (wave * kCopies + i) + (lane >> 3);
-        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-        if (8 * (wave * kCopies + i) < BN) {
-            src_off[i] = (uint32_t)((n0 + row) * a.K + chunk * 16);
-        } else {
-            int64_t mr = m0 + (row - BN);
-            mr = mr < a.M ? mr : a.M - 1;
-            src_off[i] = (uint32_t)(mr * a.K + chunk * 16);
-        }
+    for (int par = 0; par < 2; ++par) {
+        const int chunk = (lane & 7) ^ ((4 * par + (lrow >> 1)) & 7);
+        voff[par] = (uint32_t)(lrow * a.K + chunk * 16);
     }
+    // Wave-uniform row addresses of this wave's copies (scalar registers).
+    const uint8_t* cbase[kCopies];
+#pragma unroll
+    for (int c = 0; c < kCopies; ++c) {
+        const int R = 8 * (wave * kCopies + c);
+        int64_t row = R < BN ? n0 + R : m0 + (R - BN);
+        if (CLAMP && R >= BN) row = row < a.M ? row : a.M - 1;
+        cbase[c] = (R < BN ? a.w : a.x) + row * a.K;
+    }
+    auto copy_one = [&](int64_t kb, int stage, int c) {
+        const int R = 8 * (wave * kCopies + c);
+        uint32_t off = voff[c & 1];
+        if (CLAMP && R >= BN) {
+            // rows past M read row M - 1 (never stored)
+            const int64_t row = (int64_t)((cbase[c] - a.x) / a.K);
+            int64_t lr = row + lrow;
+            lr = lr < a.M ? lr : a.M - 1;
+            off = (uint32_t)((lr - row) * a.K) + (voff[c & 1] - (uint32_t)(lrow * a.K));
+        }
+        // The empty asm keeps the per-iteration scalar address opaque, so the lane
+        // offset is added at the load (scalar base + 32-bit offset) instead of being
+        // folded into a loop-invariant 64-bit address per copy.
+        const uint8_t* src = cbase[c] + kb * kGroup;
+        asm volatile("" : "+s"(src));
+        uint8_t* dst = lds + stage * kStage + (wave * kCopies + c) * 1024;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + off),
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    };
     auto copy_stage = [&](int64_t kb, int stage) {
 #pragma unroll
-        for (int i = 0; i < kCopies; ++i) {
-            const uint8_t* base = (8 * (wave * kCopies + i) < BN ? a.w : a.x) + kb * kGroup;
-            uint8_t* dst = lds + stage * kStage + (wave * kCopies + i) * 1024;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + src_off[i]),
-                                             (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-        }
+        for (int c = 0; c < kCopies; ++c) copy_one(kb, stage, c);
     };
 
     // ---- L2 warm-up of K block kb + 2: thread t touches stage row t mod (BM + BN)
@@ -134,11 +162,11 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
     static_assert(BM + BN <= kPrefillThreads, "one warm-up line per thread covers the stage");
     const int pf_row = tid % (BM + BN);
     const bool pf_w = pf_row < BN;
-    uint32_t pf_off;
+    int64_t pf_off;
     {
         int64_t row = pf_w ? n0 + pf_row : m0 + (pf_row - BN);
-        if (!pf_w) row = row < a.M ? row : a.M - 1;
-        pf_off = (uint32_t)(row * a.K);
+        if (CLAMP && !pf_w) row = row < a.M ? row : a.M - 1;
+        pf_off = row * a.K;
     }
     auto warm = [&](int64_t kb) {
         const uint8_t* base = (pf_w ? a.w : a.x) + kb * kGroup;
@@ -178,7 +206,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
     };
     bool mok[TJ];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) mok[j] = m0 + wm * WTM + 16 * j + r < a.M;
+    for (int j = 0; j < TJ; ++j) mok[j] = !CLAMP || m0 + wm * WTM + 16 * j + r < a.M;
 
     v4f acc[TI][TJ];
 #pragma unroll
@@ -204,12 +232,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
         asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (kb + 1 < a.KB) {
-            copy_stage(kb + 1, stage ^ 1);
-            copy_scales(kb + 1, stage ^ 1);
-            copy_wscales(kb + 1, stage ^ 1);
-        }
-        warm(kb + 2 < a.KB ? kb + 2 : a.KB - 1);       // always one warm-up load last
+        const bool more = kb + 1 < a.KB;
         const uint8_t* wt = lds + stage * kStage;
         const uint8_t* xt = wt + BN * 128;
         v8i bf[TJ];
@@ -225,6 +248,20 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
         v8i af_next = lds_frag(wt, wn * WTN + r, g);
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
+            // The copies of K block kb + 1 are spread over the first rows, so the
+            // workgroup's vector-memory requests do not queue up at the top of the
+            // step in front of its LDS reads; past the last K block they repeat it
+            // into the idle stage (no branch in the loop).
+            const int64_t kn = more ? kb + 1 : kb;
+            if (2 * i < kCopies) {
+                copy_one(kn, stage ^ 1, 2 * i);
+                copy_one(kn, stage ^ 1, 2 * i + 1);
+            }
+            if (2 * i + 2 == kCopies) {
+                copy_scales(kn, stage ^ 1);
+                copy_wscales(kn, stage ^ 1);
+                warm(kb + 2 < a.KB ? kb + 2 : a.KB - 1);       // always one warm-up load last
+            }
             const v8i af = af_next;
             if (i + 1 < TI) af_next = lds_frag(wt, wn * WTN + 16 * (i + 1) + r, g);
             v4f p[TJ];
@@ -264,7 +301,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
     }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, bool CLAMP>
 static hipError_t launch_tiles(PrefillArgs a, hipStream_t st) {
     a.tiles_m = (a.M + BM - 1) / BM;
     a.tiles_n = a.N / BN;
@@ -273,13 +310,20 @@ static hipError_t launch_tiles(PrefillArgs a, hipStream_t st) {
     constexpr int lds = prefill_lds_bytes(BM, BN);
     static bool attr_set = false;          // idempotent; a race only repeats the call
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)gemm_prefill_kernel<BM, BN>,
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_prefill_kernel<BM, BN, CLAMP>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((gemm_prefill_kernel<BM, BN>), dim3((unsigned)T), dim3(kPrefillThreads), lds, st, a);
+    hipLaunchKernelGGL((gemm_prefill_kernel<BM, BN, CLAMP>), dim3((unsigned)T), dim3(kPrefillThreads), lds, st, a);
     return hipGetLastError();
+}
+
+template <int BM, int BN>
+static hipError_t launch_shape(PrefillArgs a, hipStream_t st) {
+    // M < BM: one partial tile row whose rows past M are clamped.
+    if (a.M < BM) return launch_tiles<BM, BN, true>(a, st);
+    return launch_tiles<BM, BN, false>(a, st);
 }
 
 hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, const float* ws, void* y,
@@ -298,8 +342,8 @@ hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, con
     bool wide = N % 256 == 0;
     if (const char* e = getenv("FP8BS_PREFILL_TILE_N"))     // tuning hook: 128 or 256
         wide = wide && atoi(e) != 128;
-    if (wide) return launch_tiles<256, 256>(a, st);
-    return launch_tiles<256, 128>(a, st);
+    if (wide) return launch_shape<256, 256>(a, st);
+    return launch_shape<256, 128>(a, st);
 }
 
 }  // namespace fp8bs

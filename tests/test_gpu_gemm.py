@@ -51,7 +51,7 @@ def check_linear(x, w, what, workspace=None):
     return y
 
 
-SHAPES = [(M, N, K) for M in (1, 2, 5, 8, 9, 16, 17, 33, 100, 128, 129, 255, 300)
+SHAPES = [(M, N, K) for M in (1, 2, 5, 8, 9, 16, 17, 33, 100, 128, 129, 255, 256, 257, 300, 513)
           for (N, K) in ((128, 128), (384, 512), (1024, 1152))]
 
 
