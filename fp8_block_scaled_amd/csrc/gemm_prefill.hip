@@ -4,8 +4,8 @@
 // ("Nanbeige4.3-33B FP8" model card, introduction: E4M3 weights in 128x128 blocks,
 // dynamic per-token group-128 activation scales; FP32 accumulation, BF16 out).
 //
-// Tiling: a workgroup of 8 waves computes a BM (m) x BN (n) output tile, the waves
-// arranged 4 (m) x 2 (n), each owning (BM/4) x (BN/2).  The K loop steps one
+// Tiling: a workgroup of WM x WN waves (4 x 2 in the shapes launched) computes a
+// BM (m) x BN (n) output tile, each wave owning (BM/WM) x (BN/WN).  The K loop steps one
 // 128-wide scale block at a time through two LDS stages:
 //   1. at the top of step kb the wave waits for its own copies into stage kb%2
 //      and the workgroup meets at a barrier; the copies of K block kb + 1 into the
@@ -41,8 +41,6 @@
 
 namespace fp8bs {
 
-constexpr int kPrefillWaves = 8;
-constexpr int kPrefillThreads = kPrefillWaves * 64;
 constexpr int kGroupRows = 8;
 constexpr int kXcds = 8;
 
@@ -70,16 +68,22 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int g) {
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
-template <int BM, int BN, bool CLAMP>
-__global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(PrefillArgs a) {
-    constexpr int WTM = BM / 4, WTN = BN / 2;          // wave tile (m, n)
+template <int BM, int BN, int WM, int WN, bool CLAMP>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillArgs a) {
+    constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
+    constexpr int WTM = BM / WM, WTN = BN / WN;        // wave tile (m, n)
     constexpr int TJ = WTM / 16, TI = WTN / 16;         // subtiles (m, n)
     constexpr int kStage = stage_bytes(BM, BN);
-    constexpr int kCopies = (BM + BN) * 8 / kPrefillThreads;   // 16-byte copies per thread per stage
+    // A stage is (BM + BN) / 8 copy units of 8 tile rows (1 KiB, one 64-lane
+    // 16-byte direct-to-LDS load); wave w takes kUnitsLo or kUnitsLo + 1 of them.
+    constexpr int kUnits = (BM + BN) / 8;
+    constexpr int kUnitsLo = kUnits / kWaves, kUnitsExtra = kUnits % kWaves;
+    constexpr int kCopies = kUnitsLo + (kUnitsExtra ? 1 : 0);    // per wave, at most
+    constexpr int kCopyRows = (kCopies + 1) / 2;                  // subtile rows issuing copies
+    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tiles are whole MFMA subtiles");
     static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's n-range must lie in one weight block");
-    static_assert((BM + BN) * 8 % kPrefillThreads == 0, "copies must divide evenly");
-    static_assert(kCopies % 2 == 0 && BN % 8 == 0, "copies: 8-row groups, an even count per wave");
-    static_assert(kCopies / 2 <= TI, "two copies per subtile row");
+    static_assert(BN % 8 == 0 && BM % 8 == 0, "copies: 8-row groups");
+    static_assert(kCopyRows <= TI, "two copies per subtile row");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     // ---- tile selection: XCD-contiguous, grouped raster
@@ -104,19 +108,20 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int g = lane >> 4, r = lane & 15;
 
     // ---- copy assignment: stage rows [0, BN) are w rows n0.., rows [BN, BN+BM) are
-    // q rows m0..; copy c of this wave moves the 8 tile rows starting at
-    // R = 8 (wave * kCopies + c) (64 chunks, 1 KiB of LDS); lane l takes row R + l / 8
-    // and LDS chunk position l % 8, i.e. source chunk (l % 8) ^ ((row >> 1) & 7).
-    // An 8-row group lies in one operand (BN is a multiple of 8), so each copy is a
-    // wave-uniform base (row R's address) plus a 32-bit lane offset.  The lane
-    // offset depends on c only through the parity of R / 8 (the swizzle), which is
-    // the parity of c (kCopies is even): two offsets serve all copies -- except
+    // q rows m0..; copy unit u moves the 8 tile rows starting at R = 8 u (64
+    // chunks, 1 KiB of LDS at u KiB); lane l takes row R + l / 8 and LDS chunk
+    // position l % 8, i.e. source chunk (l % 8) ^ ((row >> 1) & 7).  A unit lies in
+    // one operand (BN is a multiple of 8), so each copy is a wave-uniform base (row
+    // R's address) plus a 32-bit lane offset.  The lane offset depends on u only
+    // through its parity (the swizzle): two offsets serve all copies -- except
     // with CLAMP, where rows past M are replaced by row M - 1 and the offset is
     // formed per copy.
+    const int ucount = kUnitsLo + (wave < kUnitsExtra ? 1 : 0);
+    const int ubase = wave * kUnitsLo + (wave < kUnitsExtra ? wave : kUnitsExtra);
     const int lrow = lane >> 3;
     uint32_t voff[2];
 #pragma unroll
@@ -128,27 +133,31 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
     const uint8_t* cbase[kCopies];
 #pragma unroll
     for (int c = 0; c < kCopies; ++c) {
-        const int R = 8 * (wave * kCopies + c);
+        int u = ubase + c;
+        u = u < kUnits ? u : kUnits - 1;        // an unused last slot of a short wave
+        const int R = 8 * u;
         int64_t row = R < BN ? n0 + R : m0 + (R - BN);
         if (CLAMP && R >= BN) row = row < a.M ? row : a.M - 1;
         cbase[c] = (R < BN ? a.w : a.x) + row * a.K;
     }
     auto copy_one = [&](int64_t kb, int stage, int c) {
-        const int R = 8 * (wave * kCopies + c);
-        uint32_t off = voff[c & 1];
+        if (c >= ucount) return;                // wave-uniform
+        const int u = ubase + c;
+        const int R = 8 * u;
+        uint32_t off = voff[u & 1];
         if (CLAMP && R >= BN) {
             // rows past M read row M - 1 (never stored)
             const int64_t row = (int64_t)((cbase[c] - a.x) / a.K);
             int64_t lr = row + lrow;
             lr = lr < a.M ? lr : a.M - 1;
-            off = (uint32_t)((lr - row) * a.K) + (voff[c & 1] - (uint32_t)(lrow * a.K));
+            off = (uint32_t)((lr - row) * a.K) + (voff[u & 1] - (uint32_t)(lrow * a.K));
         }
         // The empty asm keeps the per-iteration scalar address opaque, so the lane
         // offset is added at the load (scalar base + 32-bit offset) instead of being
         // folded into a loop-invariant 64-bit address per copy.
         const uint8_t* src = cbase[c] + kb * kGroup;
         asm volatile("" : "+s"(src));
-        uint8_t* dst = lds + stage * kStage + (wave * kCopies + c) * 1024;
+        uint8_t* dst = lds + stage * kStage + u * 1024;
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + off),
                                          (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     };
@@ -159,7 +168,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
 
     // ---- L2 warm-up of K block kb + 2: thread t touches stage row t mod (BM + BN)
     // (one line).  Every thread issues it, so it is always each wave's last load.
-    static_assert(BM + BN <= kPrefillThreads, "one warm-up line per thread covers the stage");
+    static_assert(BM + BN <= kThreads, "one warm-up line per thread covers the stage");
     const int pf_row = tid % (BM + BN);
     const bool pf_w = pf_row < BN;
     int64_t pf_off;
@@ -177,7 +186,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
     // ---- scales: the BM token scales and the weight-block scales of K block kb are
     // copied into the stage with the tiles (4-byte direct-to-LDS loads), so the
     // warm-up touch is always each wave's last vector load and nothing waits on it.
-    static_assert(BM % 64 == 0 && BM / 64 <= kPrefillWaves, "one scale copy per wave");
+    static_assert(BM % 64 == 0 && BM / 64 <= kWaves, "one scale copy per wave");
     const bool xs_copy = wave < BM / 64;
     uint32_t xs_off;
     {
@@ -192,10 +201,9 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
                                                                                       (BM + BN) * 128 + wave * 256),
                                              4, 0, 0);
     };
-    // Weight scales of the tile's BN/128 weight blocks: wave BM/64 copies them (lane l
-    // takes block l mod (BN/128)).
-    static_assert(BM / 64 < kPrefillWaves, "a wave is left for the weight scales");
-    const bool ws_copy = wave == BM / 64;
+    // Weight scales of the tile's BN/128 weight blocks: wave (BM/64) mod waves copies
+    // them (lane l takes block l mod (BN/128)).
+    const bool ws_copy = wave == (BM / 64) % kWaves;
     const uint32_t ws_off = (uint32_t)((n0 / kGroup + lane % (BN / kGroup)) * a.KB);
     auto copy_wscales = [&](int64_t kb, int stage) {
         if (ws_copy)
@@ -253,11 +261,11 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
             // step in front of its LDS reads; past the last K block they repeat it
             // into the idle stage (no branch in the loop).
             const int64_t kn = more ? kb + 1 : kb;
-            if (2 * i < kCopies) {
+            if (i < kCopyRows) {
                 copy_one(kn, stage ^ 1, 2 * i);
-                copy_one(kn, stage ^ 1, 2 * i + 1);
+                if (2 * i + 1 < kCopies) copy_one(kn, stage ^ 1, 2 * i + 1);
             }
-            if (2 * i + 2 == kCopies) {
+            if (i == kCopyRows - 1) {
                 copy_scales(kn, stage ^ 1);
                 copy_wscales(kn, stage ^ 1);
                 warm(kb + 2 < a.KB ? kb + 2 : a.KB - 1);       // always one warm-up load last
@@ -301,7 +309,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
     }
 }
 
-template <int BM, int BN, bool CLAMP>
+template <int BM, int BN, int WM, int WN, bool CLAMP>
 static hipError_t launch_tiles(PrefillArgs a, hipStream_t st) {
     a.tiles_m = (a.M + BM - 1) / BM;
     a.tiles_n = a.N / BN;
@@ -310,20 +318,21 @@ static hipError_t launch_tiles(PrefillArgs a, hipStream_t st) {
     constexpr int lds = prefill_lds_bytes(BM, BN);
     static bool attr_set = false;          // idempotent; a race only repeats the call
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)gemm_prefill_kernel<BM, BN, CLAMP>,
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_prefill_kernel<BM, BN, WM, WN, CLAMP>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((gemm_prefill_kernel<BM, BN, CLAMP>), dim3((unsigned)T), dim3(kPrefillThreads), lds, st, a);
+    hipLaunchKernelGGL((gemm_prefill_kernel<BM, BN, WM, WN, CLAMP>), dim3((unsigned)T), dim3(64 * WM * WN), lds,
+                       st, a);
     return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN>
 static hipError_t launch_shape(PrefillArgs a, hipStream_t st) {
     // M < BM: one partial tile row whose rows past M are clamped.
-    if (a.M < BM) return launch_tiles<BM, BN, true>(a, st);
-    return launch_tiles<BM, BN, false>(a, st);
+    if (a.M < BM) return launch_tiles<BM, BN, WM, WN, true>(a, st);
+    return launch_tiles<BM, BN, WM, WN, false>(a, st);
 }
 
 hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, const float* ws, void* y,
@@ -339,11 +348,12 @@ hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, con
     a.N = N;
     a.K = K;
     a.KB = K / kGroup;
+    // Tile shape: 256 x 256 (8 waves of 64 x 128) when N allows it, else 256 x 128
+    // (8 waves of 64 x 64).  Tuning hook FP8BS_PREFILL_TILE=128 forces the latter.
     bool wide = N % 256 == 0;
-    if (const char* e = getenv("FP8BS_PREFILL_TILE_N"))     // tuning hook: 128 or 256
-        wide = wide && atoi(e) != 128;
-    if (wide) return launch_shape<256, 256>(a, st);
-    return launch_shape<256, 128>(a, st);
+    if (const char* e = getenv("FP8BS_PREFILL_TILE")) wide = wide && atoi(e) != 128;
+    if (wide) return launch_shape<256, 256, 4, 2>(a, st);
+    return launch_shape<256, 128, 4, 2>(a, st);
 }
 
 }  // namespace fp8bs
