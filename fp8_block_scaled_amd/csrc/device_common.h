@@ -44,27 +44,42 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double d) {
     return sign | mag;
 }
 
-// E4M3 code of v, |v| <= 448, round to nearest even.  Sign from the IEEE sign bit
-// (so -0.0 and negatives that round to zero give 0x80).
-//   |v| >= 2^-6 : normal code; round the float32 mantissa to 3 bits on the bit
-//                 pattern (carry into the exponent is correct), then rebias 127 -> 7.
-//   |v| <  2^-6 : subnormal code = |v| / 2^-9 rounded to an integer; 8 becomes the
-//                 smallest normal 0x08, which is again the right code.
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-    uint32_t b = __float_as_uint(v);
-    uint32_t sign = (b >> 24) & 0x80u;
-    uint32_t a = b & 0x7FFFFFFFu;
-    uint32_t normal = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-    uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-    return (a >= 0x3C800000u ? normal : sub) | sign;
+// fl32(x / s) (IEEE division) clamped to +-448: the value a group's code encodes.
+__device__ __forceinline__ float quant_value(float x, float s) {
+    const float v = x / s;
+    return fminf(fmaxf(v, -kE4M3Max), kE4M3Max);
 }
 
-// Quantize one value by its group scale s > 0: fl32(x / s) (IEEE division), clamp
-// to +-448, encode.
-__device__ __forceinline__ uint32_t quant_one(float x, float s) {
-    float v = x / s;
-    v = fminf(fmaxf(v, -kE4M3Max), kE4M3Max);
-    return e4m3_rne(v);
+// Smallest group scale taken by quant_value_fast.
+constexpr float kFastDivMinScale = 0x1p-60f;
+
+// The same value as quant_value for s >= 2^-60, from y = fl32(1 / s) (one IEEE
+// division per group) and two correction steps with fused multiply-adds:
+//   q = fl32(|x| y);  then twice  r = fma(-q, s, |x|),  q = fma(r, y, q).
+// fl32(|x| y) is within 1.5 ulp of |x| / s; a correction step with the exactly
+// computed remainder r brings a quotient within 1.5 ulp to within 1 ulp, and from
+// within 1 ulp (with y the correctly rounded reciprocal) to the correctly rounded
+// quotient (Markstein's theorem on FMA division).  For s >= 2^-60 no step
+// underflows while |x| / s >= 2^-11; below that every code is zero anyway.  The
+// sign is taken from x at the end, so -0.0 stays -0.0.
+__device__ __forceinline__ float quant_value_fast(float x, float s, float y) {
+    const float a = fabsf(x);
+    float q = a * y;
+    float r = fmaf(-q, s, a);
+    q = fmaf(r, y, q);
+    r = fmaf(-q, s, a);
+    q = fmaf(r, y, q);
+    return copysignf(fminf(q, kE4M3Max), x);
+}
+
+// E4M3 codes of four values with |v| <= 448, packed little-endian: gfx950's
+// v_cvt_pk_fp8_f32 converts to OCP E4M3 (bias 7) with round to nearest even,
+// subnormal codes included, and takes the sign from the IEEE sign bit (-0.0 and
+// negatives that round to zero give 0x80).  Two values per instruction.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    return (uint32_t)r;
 }
 
 // DPP lane moves within rows of 16 lanes.

@@ -36,17 +36,20 @@ __device__ __forceinline__ void unpack8(const uint4& v, float (&x)[8]) {
 
 // Codes of 8 values of one group (scale s, already reduced over the group).
 __device__ __forceinline__ uint2 quant8(const float (&x)[8], float s) {
-    uint32_t c[8];
-    if (s == 0.0f) {
+    uint2 out = {0u, 0u};
+    float v[8];
+    if (s >= kFastDivMinScale) {
+        const float y = 1.0f / s;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = 0;
+        for (int i = 0; i < 8; ++i) v[i] = quant_value_fast(x[i], s, y);
+    } else if (s != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = quant_value(x[i], s);
     } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = quant_one(x[i], s);
+        return out;
     }
-    uint2 out;
-    out.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    out.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    out.x = e4m3_pack4(v[0], v[1], v[2], v[3]);
+    out.y = e4m3_pack4(v[4], v[5], v[6], v[7]);
     return out;
 }
 

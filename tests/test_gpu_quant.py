@@ -117,3 +117,32 @@ def test_quant_is_deterministic():
     for _ in range(3):
         q, s = fb.quant_act(x)
         assert torch.equal(q, ref[0]) and torch.equal(s.view(torch.int32), ref[1].view(torch.int32))
+
+
+def every_x_groups(amax_bits):
+    """Groups holding, for each amax, every BF16 magnitude in [0, amax] once (each
+    group starts with amax itself, so that is its scale); odd groups negated."""
+    rows = []
+    for a in amax_bits:
+        xs = np.arange(0, int(a) + 1, dtype=np.uint16)
+        pad = (-len(xs)) % 127
+        xs = np.concatenate([xs, np.zeros(pad, np.uint16)]).reshape(-1, 127)
+        g = np.concatenate([np.full((len(xs), 1), a, np.uint16), xs], axis=1)
+        g[1::2] |= np.uint16(0x8000)
+        rows.append(g)
+    return np.concatenate(rows)
+
+
+def test_quant_act_every_x_for_many_scales():
+    """For amax across the whole BF16 exponent range (mantissas 0x00, 0x7F and
+    random), every BF16 value up to amax, both signs: codes and scales bit-exact.
+    Covers both quotient paths (group scales below and above 2^-60)."""
+    rng = np.random.default_rng(17)
+    amax = []
+    for e in range(1, 255):                          # every biased BF16 exponent
+        for m in (0x00, 0x7F, int(rng.integers(1, 0x7F))):
+            amax.append((e << 7) | m)
+    amax += [0x0001, 0x0040, 0x007F, 0x2640, 0x2641, 0x2660, 0x2680, 0x3F80, 0x43E0, 0x4270, 0x7F7F]
+    amax = sorted(set(amax))
+    bits = every_x_groups(np.array(amax, np.uint16))
+    check_quant(bits, f"every x for {len(amax)} scales")
