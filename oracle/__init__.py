@@ -20,6 +20,7 @@ Modules
              saturation (table + midpoint search).
   quant   -- per-token group-128 activation quantizer, 128x128 block weight
              quantizer, SiLU(gate)*up in float64 rounded once to BF16.
+  rmsnorm -- RMSNorm in float64 rounded once to BF16, then the quantizer.
   linear  -- dequantize-and-matmul in float64 and the output tolerance check.
 
 Parity pins (tests/test_oracle_*.py) tie every function to something other than
@@ -37,6 +38,7 @@ from .quant import (  # noqa: F401
     silu_mul_bf16,
     silu_mul_quant,
 )
+from .rmsnorm import rmsnorm_bf16, rmsnorm_quant  # noqa: F401
 from .linear import (  # noqa: F401
     dequant_act,
     dequant_weight,

@@ -8,9 +8,11 @@ import oracle
 import oracle.e4m3 as e4m3
 import oracle.linear as linear
 import oracle.quant as quant
+import oracle.rmsnorm as rmsnorm
 from tests import test_oracle_e4m3 as te
 from tests import test_oracle_linear as tl
 from tests import test_oracle_quant as tq
+from tests import test_oracle_rmsnorm as tr
 from tests import test_oracle_silu as ts
 
 
@@ -82,6 +84,23 @@ def _silu_via_f32(gu_bits):
     return quant.f64_to_bf16_bits(r.astype(np.float64))   # double rounding
 
 
+def _rmsnorm_variant(sum_not_mean=False, eps_outside=False, round_normalized=False):
+    def f(x_bits, gamma_bits, eps):
+        x = quant.bf16_bits_to_f32(np.asarray(x_bits, np.uint16)).astype(np.float64)
+        g = quant.bf16_bits_to_f32(np.asarray(gamma_bits, np.uint16)).astype(np.float64)
+        ms = np.sum(x * x, axis=1, keepdims=True)
+        if not sum_not_mean:
+            ms = ms / x.shape[1]
+        e = float(np.float32(eps))
+        r = 1.0 / np.sqrt(ms) + e if eps_outside else 1.0 / np.sqrt(ms + e)
+        n = x * r
+        if round_normalized:                                  # BF16(BF16(x r) * gamma)
+            n = quant.bf16_bits_to_f32(quant.f64_to_bf16_bits(n)).astype(np.float64)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            return quant.f64_to_bf16_bits(n * g)
+    return f
+
+
 MUTATIONS = {
     "ties_away_from_zero": ([(e4m3, "encode_rne_sat", _encode_ties_away), (quant, "encode_rne_sat", _encode_ties_away),
                              (oracle, "encode_rne_sat", _encode_ties_away)],
@@ -100,6 +119,15 @@ MUTATIONS = {
                   [ts.test_silu_special_values]),
     "silu_double_rounding": ([(quant, "silu_mul_bf16", _silu_via_f32), (oracle, "silu_mul_bf16", _silu_via_f32)],
                              [ts.test_silu_mul_matches_high_precision_reference, ts.test_silu_mul_near_rounding_midpoints]),
+    "rmsnorm_sum_not_mean": ([(rmsnorm, "rmsnorm_bf16", _rmsnorm_variant(sum_not_mean=True)),
+                              (oracle, "rmsnorm_bf16", _rmsnorm_variant(sum_not_mean=True))],
+                             [tr.test_rmsnorm_matches_exact_decimal]),
+    "rmsnorm_eps_outside_root": ([(rmsnorm, "rmsnorm_bf16", _rmsnorm_variant(eps_outside=True)),
+                                  (oracle, "rmsnorm_bf16", _rmsnorm_variant(eps_outside=True))],
+                                 [tr.test_rmsnorm_matches_exact_decimal, tr.test_rmsnorm_closed_forms]),
+    "rmsnorm_double_rounding": ([(rmsnorm, "rmsnorm_bf16", _rmsnorm_variant(round_normalized=True)),
+                                 (oracle, "rmsnorm_bf16", _rmsnorm_variant(round_normalized=True))],
+                                [tr.test_rmsnorm_matches_exact_decimal]),
 }
 
 
