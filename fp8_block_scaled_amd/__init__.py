@@ -9,6 +9,7 @@ outputs and pass raw pointers.
     qw, ws = quant_weight(w)                  # w: bf16 [N, K]
     y = block_linear(q, s, qw, ws)            # y: bf16 [M, N]
     q2, s2 = silu_mul_quant(gu)               # gu: bf16 [M, 2I] -> codes of BF16(silu(g)*u)
+    q3, s3 = rmsnorm_quant(x, gamma, 1e-5)    # codes of BF16(RMSNorm(x) * gamma)
 
 Tensor dtypes: BF16 tensors are torch.bfloat16; E4M3 codes are torch.uint8 (view
 them as torch.float8_e4m3fn if wanted); scales are torch.float32.
@@ -22,6 +23,7 @@ __all__ = [
     "quant_act",
     "quant_weight",
     "silu_mul_quant",
+    "rmsnorm_quant",
     "block_linear",
     "workspace_size",
     "get_workspace",
@@ -88,6 +90,22 @@ def silu_mul_quant(gu, q=None, s=None):
     q = torch.empty((M, I), dtype=torch.uint8, device=gu.device) if q is None else q
     s = torch.empty((M, I // 128), dtype=torch.float32, device=gu.device) if s is None else s
     _call("fp8_silu_mul_quant", gu.device, gu.data_ptr(), q.data_ptr(), s.data_ptr(), M, I)
+    return q, s
+
+
+def rmsnorm_quant(x, gamma, eps, q=None, s=None):
+    """Codes and scales of BF16(x / sqrt(mean(x^2) + eps) * gamma) for BF16 x [M, K]
+    and gamma [K] (FP64 evaluation, one BF16 rounding), quantized per token and group."""
+    _check_tensor(x, "x", _BF16, 2)
+    _check_tensor(gamma, "gamma", _BF16, 1)
+    M, K = x.shape
+    if gamma.shape[0] != K:
+        raise ValueError("gamma must have K elements")
+    if gamma.device != x.device:
+        raise ValueError("x and gamma must be on the same device")
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
+    s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if s is None else s
+    _call("fp8_rmsnorm_quant", x.device, x.data_ptr(), gamma.data_ptr(), float(eps), q.data_ptr(), s.data_ptr(), M, K)
     return q, s
 
 

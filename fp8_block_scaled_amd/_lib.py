@@ -20,6 +20,7 @@ STATUS_NAMES = {
     -4: "FP8BS_ERR_DEVICE",
     -5: "FP8BS_ERR_HIP",
     -6: "FP8BS_ERR_WORKSPACE",
+    -7: "FP8BS_ERR_VALUE",
 }
 
 # Every symbol the header declares, with (restype, argtypes).
@@ -29,6 +30,7 @@ SIGNATURES = {
     "fp8_quant_act": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "fp8_quant_weight": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "fp8_silu_mul_quant": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "fp8_rmsnorm_quant": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, _P, _I64, _I64, _P]),
     "fp8_block_linear": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "fp8_block_linear_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "fp8bs_status_string": (ctypes.c_char_p, [ctypes.c_int]),

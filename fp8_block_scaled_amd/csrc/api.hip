@@ -6,6 +6,7 @@
 // is gfx950, and enqueues the kernels on the caller's stream.
 #include <atomic>
 #include <cstdint>
+#include <cmath>
 #include <cstring>
 
 #include "fp8bs.h"
@@ -64,6 +65,7 @@ const char* fp8bs_status_string(int status) {
         case FP8BS_ERR_DEVICE: return "the current HIP device is not gfx950 (MI355X)";
         case FP8BS_ERR_HIP: return "HIP runtime call or kernel launch failed";
         case FP8BS_ERR_WORKSPACE: return "workspace must be 256-byte aligned";
+        case FP8BS_ERR_VALUE: return "scalar argument out of range (eps must be finite and > 0)";
         default: return "unknown fp8bs status";
     }
 }
@@ -90,6 +92,17 @@ int fp8_silu_mul_quant(const void* gu_bf16, void* q_e4m3, float* s_f32, int64_t 
     if (rc != FP8BS_OK) return rc > 0 ? FP8BS_OK : rc;
     if ((rc = check_device(nullptr)) != FP8BS_OK) return rc;
     return hip_status(fp8bs::launch_silu_mul_quant(gu_bf16, q_e4m3, s_f32, M, I, stream));
+}
+
+int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, float eps, void* q_e4m3, float* s_f32,
+                      int64_t M, int64_t K, hipStream_t stream) {
+    int rc = quant_shape_check(x_bf16, q_e4m3, s_f32, M, K);
+    if (rc != FP8BS_OK) return rc > 0 ? FP8BS_OK : rc;
+    if (!gamma_bf16) return FP8BS_ERR_NULL;
+    if (!aligned(gamma_bf16, 16)) return FP8BS_ERR_ALIGN;
+    if (!(eps > 0.0f) || !std::isfinite(eps)) return FP8BS_ERR_VALUE;
+    if ((rc = check_device(nullptr)) != FP8BS_OK) return rc;
+    return hip_status(fp8bs::launch_rmsnorm_quant(x_bf16, gamma_bf16, eps, q_e4m3, s_f32, M, K, stream));
 }
 
 size_t fp8_block_linear_workspace_size(int64_t M, int64_t N, int64_t K) {

@@ -10,6 +10,8 @@ namespace fp8bs {
 
 hipError_t launch_quant_act(const void* x, void* q, float* s, int64_t M, int64_t K, hipStream_t st);
 hipError_t launch_silu_mul_quant(const void* gu, void* q, float* s, int64_t M, int64_t I, hipStream_t st);
+hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, float eps, void* q, float* s, int64_t M, int64_t K,
+                                hipStream_t st);
 hipError_t launch_quant_weight(const void* w, void* qw, float* ws, int64_t N, int64_t K, hipStream_t st);
 
 // ---- decode GEMM (M <= kDecodeMaxM): one workgroup per strip of `rows` columns, split-K over its waves

@@ -2,6 +2,7 @@
 //   quant_act_kernel       dynamic per-token, group-128 activation quantization
 //   silu_mul_quant_kernel  h = BF16(silu(gate) * up) in FP64, then the same quantization
 //   quant_weight_kernel    128x128 block weight quantization (offline step)
+//   rmsnorm_quant_kernel   h = BF16(RMSNorm(x) * gamma) in float64, then the same quantization
 //
 // Scheme: "Nanbeige4.3-33B FP8" model card, introduction and "Recipe and
 // calibration" (E4M3 weights in 128x128 blocks, minmax scales; dynamic per-token
@@ -155,6 +156,63 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) dst[i] = quant8(v[i], sc);
     if (t == 0) ws[blockIdx.x] = sc;
+}
+
+// RMSNorm + quantization, one workgroup per row m of x [M, K]:
+//   1. the row's sum of squares in float64 (x^2 is exact for BF16 x): each thread
+//      over 16-byte chunks, then the wave (shuffles) and the workgroup (LDS, fixed
+//      order, so the result is deterministic);  r = 1 / sqrt(sum / K + eps);
+//   2. per 128-group, one 16-lane DPP row: h = BF16((x r) gamma) evaluated in
+//      float64 and rounded once, then the group's amax, scale and codes as in
+//      quant_act_kernel.
+// The row is read twice; the second read finds it in the cache.
+constexpr int kNormThreads = 256;
+
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, double eps, uint8_t* __restrict__ q,
+    float* __restrict__ s, int64_t K) {
+    __shared__ double part[kNormThreads / 64];
+    const int64_t m = blockIdx.x;
+    const uint16_t* xr = x + m * K;
+    const int64_t chunks = K / 8;
+    double ss = 0.0;
+    for (int64_t c = threadIdx.x; c < chunks; c += kNormThreads) {
+        float v[8];
+        unpack8(reinterpret_cast<const uint4*>(xr)[c], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += (double)v[i] * (double)v[i];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    double total = 0.0;
+#pragma unroll
+    for (int w = 0; w < kNormThreads / 64; ++w) total += part[w];
+    const double r = 1.0 / sqrt(total / (double)K + eps);
+
+    const int grow = threadIdx.x >> 4;
+    const int sub = threadIdx.x & 15;
+    const int64_t groups = K / kGroup;
+    for (int64_t j = grow; j < groups; j += kNormThreads / 16) {     // uniform over the 16-lane row
+        float xf[8], gf[8], h[8];
+        unpack8(reinterpret_cast<const uint4*>(xr + j * kGroup)[sub], xf);
+        unpack8(reinterpret_cast<const uint4*>(gamma + j * kGroup)[sub], gf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = bf16_to_f32(f64_to_bf16_rne(((double)xf[i] * r) * (double)gf[i]));
+        const float amax = row16_max(absmax8(h));
+        const float sc = amax / kE4M3Max;
+        reinterpret_cast<uint2*>(q + m * K + j * kGroup)[sub] = quant8(h, sc);
+        if (sub == 0) s[m * groups + j] = sc;
+    }
+}
+
+hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, float eps, void* q, float* s, int64_t M, int64_t K,
+                                hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3((unsigned)M), dim3(kNormThreads), 0, st, (const uint16_t*)x,
+                       (const uint16_t*)gamma, (double)eps, (uint8_t*)q, s, K);
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_act(const void* x, void* q, float* s, int64_t M, int64_t K, hipStream_t st) {

@@ -43,7 +43,8 @@ typedef enum {
     FP8BS_ERR_ALIGN = -3,     /* a pointer violates the alignment rule above      */
     FP8BS_ERR_DEVICE = -4,    /* the current device is not gfx950                 */
     FP8BS_ERR_HIP = -5,       /* a HIP runtime call or a kernel launch failed     */
-    FP8BS_ERR_WORKSPACE = -6  /* workspace given but misaligned                   */
+    FP8BS_ERR_WORKSPACE = -6, /* workspace given but misaligned                   */
+    FP8BS_ERR_VALUE = -7      /* a scalar argument out of range (eps <= 0, NaN)   */
 } fp8bs_status;
 
 /*
@@ -83,6 +84,24 @@ int fp8_silu_mul_quant(const void* gu_bf16, void* q_e4m3, float* s_f32,
                        int64_t M, int64_t I, hipStream_t stream);
 
 /*
+ * Input of the q/k/v projection: h = BF16(RMSNorm(x) * gamma), then the activation
+ * quantization above applied to h ("Nanbeige4.3-33B DMS sidecar" card, "Format and
+ * hipEngine compatibility": the normalized stage before the q projection;
+ * "Nanbeige4.3-33B DFlash2" card, architecture table: RMS epsilon 1e-5).
+ *   x_bf16     [M, K]      hidden states (in).
+ *   gamma_bf16 [K]         RMSNorm weight (in), 16-byte aligned.
+ *   eps                    added to the mean square; finite and > 0, else
+ *                          FP8BS_ERR_VALUE.
+ *   q_e4m3     [M, K]      E4M3 codes of h (out).
+ *   s_f32      [M, K/128]  scales of h (out).
+ * h[m, k] = x[m, k] / sqrt(mean_k x[m, k]^2 + eps) * gamma[k], evaluated in FP64
+ * (eps widened exactly) and rounded to BF16 once (nearest even).  K must be a
+ * multiple of 128.  Deterministic.
+ */
+int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, float eps,
+                      void* q_e4m3, float* s_f32, int64_t M, int64_t K, hipStream_t stream);
+
+/*
  * Block-scaled FP8 GEMM: y = (q * s) @ (w * ws)^T, accumulated in FP32, stored BF16.
  *   q_e4m3  [M, K]            activation codes; s_f32 [M, K/128] their scales.
  *   w_e4m3  [N, K]            weight codes;     ws_f32 [N/128, K/128] block scales.
@@ -115,7 +134,7 @@ const char* fp8bs_status_string(int status);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int fp8bs_abi_version(void);
 
-#define FP8BS_ABI_VERSION 10000
+#define FP8BS_ABI_VERSION 10100
 
 #ifdef __cplusplus
 }

@@ -37,6 +37,7 @@ from .gen import (  # noqa: F401
     TID_ROWS,
     TID_GU,
     TID_W_DOWN,
+    TID_GAMMA,
     f32_to_bf16_bits,
     normal_rows,
     bf16_normal,

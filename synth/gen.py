@@ -13,6 +13,7 @@ TID_ZERO = 3
 TID_ROWS = 4
 TID_GU = 5
 TID_W_DOWN = 6
+TID_GAMMA = 7          # RMSNorm weight vector
 
 
 def _rng(seed, tid, row):

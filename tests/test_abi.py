@@ -12,7 +12,7 @@ from fp8_block_scaled_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp8bs.h")
 
-OK, ENULL, ESHAPE, EALIGN, EDEV, EHIP, EWS = 0, -1, -2, -3, -4, -5, -6
+OK, ENULL, ESHAPE, EALIGN, EDEV, EHIP, EWS, EVAL = 0, -1, -2, -3, -4, -5, -6, -7
 # Fake, never-dereferenced addresses: validation must reject before using them.
 A16, A16b, A16c, A16d, A16e = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
 
@@ -40,8 +40,8 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8bs_abi_version() == 10000
-    for st in (OK, ENULL, ESHAPE, EALIGN, EDEV, EHIP, EWS):
+    assert L.fp8bs_abi_version() == 10100
+    for st in (OK, ENULL, ESHAPE, EALIGN, EDEV, EHIP, EWS, EVAL):
         assert L.fp8bs_status_string(st)
     assert b"unknown" in L.fp8bs_status_string(12345)
 
@@ -64,6 +64,18 @@ def test_weight_and_silu_validation(L):
     assert L.fp8_silu_mul_quant(A16, A16b, A16c, 2, 100, None) == ESHAPE
     assert L.fp8_silu_mul_quant(A16, None, A16c, 2, 128, None) == ENULL
     assert L.fp8_silu_mul_quant(A16, A16b, A16c, 0, 128, None) == OK
+
+
+def test_rmsnorm_quant_validation(L):
+    f = L.fp8_rmsnorm_quant
+    assert f(A16, A16b, 1e-5, A16c, A16d, 4, 200, None) == ESHAPE
+    assert f(A16, None, 1e-5, A16c, A16d, 4, 128, None) == ENULL
+    assert f(A16, A16b + 2, 1e-5, A16c, A16d, 4, 128, None) == EALIGN
+    assert f(A16, A16b, 0.0, A16c, A16d, 4, 128, None) == EVAL
+    assert f(A16, A16b, -1e-5, A16c, A16d, 4, 128, None) == EVAL
+    assert f(A16, A16b, float("nan"), A16c, A16d, 4, 128, None) == EVAL
+    assert f(A16, A16b, float("inf"), A16c, A16d, 4, 128, None) == EVAL
+    assert f(None, None, 1e-5, None, None, 0, 128, None) == OK        # empty: no-op
 
 
 def test_block_linear_validation(L):

@@ -146,3 +146,47 @@ def test_quant_act_every_x_for_many_scales():
     amax = sorted(set(amax))
     bits = every_x_groups(np.array(amax, np.uint16))
     check_quant(bits, f"every x for {len(amax)} scales")
+
+
+def check_rmsnorm(x, g, eps, what):
+    banner(f"rmsnorm_quant {what} shape={x.shape}")
+    q, s = fb.rmsnorm_quant(dev_bf16(x), dev_bf16(g), eps)
+    torch.cuda.synchronize()
+    qo, so = oracle.rmsnorm_quant(x, g, eps)
+    assert_bits_equal(host_f32(s), so, f"{what} scales")
+    assert_bits_equal(host_u8(q), qo, f"{what} codes")
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (1, 7168), (5, 384), (37, 2048), (300, 1024), (8, 21504)])
+def test_rmsnorm_quant_random(M, K):
+    rng = np.random.default_rng(M * 7 + K)
+    x = bf16(rng.standard_normal((M, K)) * 10.0 ** rng.integers(-3, 4, (M, 1)))
+    g = bf16(rng.standard_normal(K) * 0.3 + 1.0)
+    check_rmsnorm(x, g, np.float32(1e-5), "random")
+
+
+def test_rmsnorm_quant_edge_rows():
+    rng = np.random.default_rng(3)
+    K = 1024
+    x = bf16(rng.standard_normal((8, K)))
+    x[0] = 0                                   # zero row -> all scales 0
+    x[1] = 0x8000                              # -0.0 row
+    x[2, :] = 0x0001                           # smallest subnormal: eps dominates
+    x[3, :] = bf16(np.float32(3e38))           # largest magnitudes (x^2 in float64)
+    x[4, 5] = bf16(np.float32(1e4))            # one spike: other groups near zero
+    x[5, 128:256] = 0                          # one zero group in a normal row
+    g = bf16(rng.standard_normal(K))
+    g[:128] = 0                                # zero weights -> zero group
+    check_rmsnorm(x, g, np.float32(1e-5), "edge rows")
+    check_rmsnorm(x, g, np.float32(1.0), "edge rows, eps 1")
+
+
+def test_rmsnorm_quant_workload_rows():
+    """The decode shape (one token, K = 7168) and 64 rows of the prefill shape."""
+    wl = synth.WORKLOADS["decode_qkv"]
+    x = synth.make_activation(wl)
+    g = bf16(oracle.bf16_bits_to_f32(synth.bf16_normal(1, wl.K, 0.1, wl.seed, synth.TID_GAMMA)[0]) + 1.0)
+    check_rmsnorm(x, g, np.float32(1e-5), "decode_qkv")
+    wp = synth.WORKLOADS["prefill_oproj"]
+    rows = synth.activation_rows(wp, np.arange(64) * 127)
+    check_rmsnorm(rows, g, np.float32(1e-5), "prefill_oproj rows")
