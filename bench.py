@@ -183,6 +183,37 @@ def time_case(case, steps, warmup):
     return ms_step, gemm_us, quant_us
 
 
+def time_rmsnorm_quant(wl, steps):
+    """Average duration of fp8_rmsnorm_quant on the workload's activations (graph-timed)
+    and its HBM roofline: read x and gamma, write codes and scales."""
+    import numpy as np
+    import torch
+    import fp8_block_scaled_amd as fb
+    import synth
+    from synth.gen import f32_to_bf16_bits
+    M, K = wl.M, wl.K
+    x = torch.from_numpy(synth.make_activation(wl).view(np.int16)).cuda()
+    g = synth.bf16_normal(1, K, 0.1, wl.seed, synth.TID_GAMMA)[0]
+    g = f32_to_bf16_bits(((g.astype(np.uint32) << 16).view(np.float32) + 1.0).astype(np.float32))
+    g = torch.from_numpy(g.view(np.int16)).cuda()
+    q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    s = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        fb.rmsnorm_quant(x, g, 1e-5, q, s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            fb.rmsnorm_quant(x, g, 1e-5, q, s)
+    graph.replay()
+    us = _replay_ms(graph) * 1e3 / steps
+    nbytes = 2 * M * K + 2 * K + M * K + 4 * M * (K // 128)
+    achieved = nbytes / (us * 1e-6) / 1e9
+    return {"M": M, "K": K, "us": round(us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4)}}
+
+
 def roofline_for(wl, gemm_us, traffic):
     if wl.M <= 16:
         achieved = wl.gemm_bytes() / (gemm_us * 1e-6) / 1e9
@@ -401,6 +432,9 @@ def main():
             del c2
             torch.cuda.empty_cache()
         out["workloads"] = others
+        print("[bench] rmsnorm_quant", file=sys.stderr, flush=True)
+        out["rmsnorm_quant"] = {name: time_rmsnorm_quant(WORKLOADS[name], 50 if name == "prefill_oproj" else 200)
+                                for name in ("decode_qkv", "prefill_oproj")}
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -2,7 +2,7 @@
 //   quant_act_kernel       dynamic per-token, group-128 activation quantization
 //   silu_mul_quant_kernel  h = BF16(silu(gate) * up) in FP64, then the same quantization
 //   quant_weight_kernel    128x128 block weight quantization (offline step)
-//   rmsnorm_quant_kernel   h = BF16(RMSNorm(x) * gamma) in float64, then the same quantization
+//   rmsnorm_quant_kernel   h = BF16(RMSNorm(x) * gamma), rounded once, then the same quantization
 //
 // Scheme: "Nanbeige4.3-33B FP8" model card, introduction and "Recipe and
 // calibration" (E4M3 weights in 128x128 blocks, minmax scales; dynamic per-token
@@ -158,29 +158,90 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(
     if (t == 0) ws[blockIdx.x] = sc;
 }
 
-// RMSNorm + quantization, one workgroup per row m of x [M, K]:
-//   1. the row's sum of squares in float64 (x^2 is exact for BF16 x): each thread
-//      over 16-byte chunks, then the wave (shuffles) and the workgroup (LDS, fixed
-//      order, so the result is deterministic);  r = 1 / sqrt(sum / K + eps);
-//   2. per 128-group, one 16-lane DPP row: h = BF16((x r) gamma) evaluated in
-//      float64 and rounded once, then the group's amax, scale and codes as in
-//      quant_act_kernel.
-// The row is read twice; the second read finds it in the cache.
+// RMSNorm + quantization, one workgroup per row m of x [M, K].  Thread (grow, sub)
+// -- 16-lane DPP row grow, lane sub -- owns 16-byte chunk sub of the row's groups
+// grow, grow + 16, ...:
+//   1. it loads those chunks of x and gamma (kept in registers when the row fits,
+//      U chunks per thread) and sums the squares of x in float64 (x^2 is exact for
+//      BF16 x); the wave (shuffles) and the workgroup (LDS, fixed order, so the
+//      result is deterministic) reduce;  r = 1 / sqrt(sum / K + eps);
+//   2. per group: h = BF16((x r) gamma), the BF16 rounding of the float64 value
+//      (decided in float32 where that is provably the same), then the group's
+//      amax, scale and codes as in quant_act_kernel.
+// U = 0 is the general form for long rows: x and gamma are read again in step 2
+// (from cache).
 constexpr int kNormThreads = 256;
+constexpr int kNormRowsPerPass = kNormThreads / 16;      // groups in flight per pass
 
+// h = BF16((x r) gamma) for 8 values, exactly rounded.  Float32 first:
+// h32 = fl32(fl32(x r32) gamma) is within 4 float32 ulps of the exact product, so its
+// BF16 rounding is the exact one unless h32 lies within 8 ulps of a BF16 rounding
+// midpoint (low 16 bits near 0x8000) or in the BF16 subnormal range; those
+// elements (rare) are redone in float64.
+__device__ __forceinline__ void rmsnorm8(const float (&xf)[8], const float (&gf)[8], double r, float r32,
+                                         float (&h)[8]) {
+    uint32_t hb[8];
+    bool redo = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float h32 = (xf[i] * r32) * gf[i];
+        const uint32_t b = __float_as_uint(h32);
+        const uint32_t a = b & 0x7FFFFFFFu;
+        hb[i] = f32_to_bf16_rne(h32);
+        redo |= ((b & 0xFFFFu) - 0x7FF8u) < 0x10u || (a != 0u && a < 0x03800000u);
+    }
+    if (redo) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t b = __float_as_uint((xf[i] * r32) * gf[i]);
+            const uint32_t a = b & 0x7FFFFFFFu;
+            if (((b & 0xFFFFu) - 0x7FF8u) < 0x10u || (a != 0u && a < 0x03800000u))
+                hb[i] = f64_to_bf16_rne(((double)xf[i] * r) * (double)gf[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = bf16_to_f32(hb[i]);
+}
+
+template <int U>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, double eps, uint8_t* __restrict__ q,
     float* __restrict__ s, int64_t K) {
     __shared__ double part[kNormThreads / 64];
     const int64_t m = blockIdx.x;
     const uint16_t* xr = x + m * K;
-    const int64_t chunks = K / 8;
+    const int grow = threadIdx.x >> 4;
+    const int sub = threadIdx.x & 15;
+    const int64_t groups = K / kGroup;
+    constexpr int UR = U > 0 ? U : 1;
+    uint4 xraw[UR], graw[UR];
     double ss = 0.0;
-    for (int64_t c = threadIdx.x; c < chunks; c += kNormThreads) {
-        float v[8];
-        unpack8(reinterpret_cast<const uint4*>(xr)[c], v);
+    if (U > 0) {
+        // x and gamma chunks requested together, before the reduction
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ss += (double)v[i] * (double)v[i];
+        for (int u = 0; u < UR; ++u) {
+            const int64_t j = grow + kNormRowsPerPass * u;
+            if (j < groups) {
+                xraw[u] = reinterpret_cast<const uint4*>(xr + j * kGroup)[sub];
+                graw[u] = reinterpret_cast<const uint4*>(gamma + j * kGroup)[sub];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int64_t j = grow + kNormRowsPerPass * u;
+            if (j >= groups) continue;
+            float v[8];
+            unpack8(xraw[u], v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss += (double)v[i] * (double)v[i];
+        }
+    } else {
+        for (int64_t j = grow; j < groups; j += kNormRowsPerPass) {
+            float v[8];
+            unpack8(reinterpret_cast<const uint4*>(xr + j * kGroup)[sub], v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss += (double)v[i] * (double)v[i];
+        }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
@@ -190,28 +251,51 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
 #pragma unroll
     for (int w = 0; w < kNormThreads / 64; ++w) total += part[w];
     const double r = 1.0 / sqrt(total / (double)K + eps);
+    const float r32 = (float)r;
 
-    const int grow = threadIdx.x >> 4;
-    const int sub = threadIdx.x & 15;
-    const int64_t groups = K / kGroup;
-    for (int64_t j = grow; j < groups; j += kNormThreads / 16) {     // uniform over the 16-lane row
+    auto emit = [&](int64_t j, const uint4& xv, const uint4& gv) {      // uniform over the 16-lane row
         float xf[8], gf[8], h[8];
-        unpack8(reinterpret_cast<const uint4*>(xr + j * kGroup)[sub], xf);
-        unpack8(reinterpret_cast<const uint4*>(gamma + j * kGroup)[sub], gf);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = bf16_to_f32(f64_to_bf16_rne(((double)xf[i] * r) * (double)gf[i]));
+        unpack8(xv, xf);
+        unpack8(gv, gf);
+        rmsnorm8(xf, gf, r, r32, h);
         const float amax = row16_max(absmax8(h));
         const float sc = amax / kE4M3Max;
         reinterpret_cast<uint2*>(q + m * K + j * kGroup)[sub] = quant8(h, sc);
         if (sub == 0) s[m * groups + j] = sc;
+    };
+    if (U > 0) {
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int64_t j = grow + kNormRowsPerPass * u;
+            if (j < groups) emit(j, xraw[u], graw[u]);
+        }
+    } else {
+        for (int64_t j = grow; j < groups; j += kNormRowsPerPass)
+            emit(j, reinterpret_cast<const uint4*>(xr + j * kGroup)[sub],
+                 reinterpret_cast<const uint4*>(gamma + j * kGroup)[sub]);
     }
 }
 
 hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, float eps, void* q, float* s, int64_t M, int64_t K,
                                 hipStream_t st) {
     if (M == 0) return hipSuccess;
-    hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3((unsigned)M), dim3(kNormThreads), 0, st, (const uint16_t*)x,
-                       (const uint16_t*)gamma, (double)eps, (uint8_t*)q, s, K);
+    const int64_t passes = (K / kGroup + kNormRowsPerPass - 1) / kNormRowsPerPass;
+    const dim3 grid((unsigned)M), block(kNormThreads);
+    const uint16_t* xp = (const uint16_t*)x;
+    const uint16_t* gp = (const uint16_t*)gamma;
+    const double e = (double)eps;
+    if (passes <= 1)
+        hipLaunchKernelGGL(rmsnorm_quant_kernel<1>, grid, block, 0, st, xp, gp, e, (uint8_t*)q, s, K);
+    else if (passes <= 2)
+        hipLaunchKernelGGL(rmsnorm_quant_kernel<2>, grid, block, 0, st, xp, gp, e, (uint8_t*)q, s, K);
+    else if (passes <= 4)
+        hipLaunchKernelGGL(rmsnorm_quant_kernel<4>, grid, block, 0, st, xp, gp, e, (uint8_t*)q, s, K);
+    else if (passes <= 8)
+        hipLaunchKernelGGL(rmsnorm_quant_kernel<8>, grid, block, 0, st, xp, gp, e, (uint8_t*)q, s, K);
+    else if (passes <= 16)
+        hipLaunchKernelGGL(rmsnorm_quant_kernel<16>, grid, block, 0, st, xp, gp, e, (uint8_t*)q, s, K);
+    else
+        hipLaunchKernelGGL(rmsnorm_quant_kernel<0>, grid, block, 0, st, xp, gp, e, (uint8_t*)q, s, K);
     return hipGetLastError();
 }
 

@@ -157,7 +157,8 @@ def check_rmsnorm(x, g, eps, what):
     assert_bits_equal(host_u8(q), qo, f"{what} codes")
 
 
-@pytest.mark.parametrize("M,K", [(1, 128), (1, 7168), (5, 384), (37, 2048), (300, 1024), (8, 21504)])
+@pytest.mark.parametrize("M,K", [(1, 128), (1, 7168), (5, 384), (37, 2048), (300, 1024), (8, 21504), (2000, 1024),
+                                 (3, 4096), (2, 8192), (2, 33024)])
 def test_rmsnorm_quant_random(M, K):
     rng = np.random.default_rng(M * 7 + K)
     x = bf16(rng.standard_normal((M, K)) * 10.0 ** rng.integers(-3, 4, (M, 1)))
