@@ -132,6 +132,10 @@ int fp8_block_linear(const void* q_e4m3, const float* s_f32, const void* w_e4m3,
         return hip_status(
             fp8bs::launch_gemm_decode(plan, q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, stream));
     }
+    if (M <= fp8bs::kMidMaxM) {
+        const fp8bs::MidPlan plan = fp8bs::plan_mid(M, N, K, cus);
+        return hip_status(fp8bs::launch_gemm_mid(plan, q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, stream));
+    }
     return hip_status(fp8bs::launch_gemm_prefill(q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, cus, stream));
 }
 

@@ -337,7 +337,6 @@ static hipError_t launch_shape(PrefillArgs a, hipStream_t st) {
 
 hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, const float* ws, void* y,
                                int64_t M, int64_t N, int64_t K, int cus, hipStream_t st) {
-    (void)cus;
     PrefillArgs a;
     a.w = (const uint8_t*)w;
     a.ws = ws;
@@ -348,12 +347,28 @@ hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, con
     a.N = N;
     a.K = K;
     a.KB = K / kGroup;
-    // Tile shape: 256 x 256 (8 waves of 64 x 128) when N allows it, else 256 x 128
-    // (8 waves of 64 x 64).  Tuning hook FP8BS_PREFILL_TILE=128 forces the latter.
-    bool wide = N % 256 == 0;
-    if (const char* e = getenv("FP8BS_PREFILL_TILE")) wide = wide && atoi(e) != 128;
-    if (wide) return launch_shape<256, 256, 4, 2>(a, st);
-    return launch_shape<256, 128, 4, 2>(a, st);
+    // Tile shape, 8 waves each: the largest of 256 x 256 (waves of 64 x 128),
+    // 128 x 256 and 128 x 128 that still gives nearly every CU a tile (measured on
+    // M = 129 .. 8191, N = K = 7168: a tile row of 256 wins only when there are
+    // enough tiles to fill the GPU).  Tuning hook FP8BS_PREFILL_TILE = 256256,
+    // 256128, 128256 or 128128 forces a shape.
+    const bool n256 = N % 256 == 0;
+    const int64_t enough = cus - cus / 8;
+    auto tiles = [&](int64_t bm, int64_t bn) { return (M + bm - 1) / bm * (N / bn); };
+    int tile = 128128;
+    if (n256 && tiles(256, 256) >= enough) tile = 256256;
+    else if (n256 && tiles(128, 256) >= enough) tile = 128256;
+    else if (!n256 && tiles(256, 128) >= enough) tile = 256128;
+    if (const char* e = getenv("FP8BS_PREFILL_TILE")) {
+        const int t = atoi(e);
+        if (t == 256128 || t == 128128 || (n256 && (t == 256256 || t == 128256))) tile = t;
+    }
+    switch (tile) {
+        case 256256: return launch_shape<256, 256, 4, 2>(a, st);
+        case 128256: return launch_shape<128, 256, 2, 4>(a, st);
+        case 128128: return launch_shape<128, 128, 2, 4>(a, st);
+        default: return launch_shape<256, 128, 4, 2>(a, st);
+    }
 }
 
 }  // namespace fp8bs

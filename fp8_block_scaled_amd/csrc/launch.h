@@ -31,7 +31,25 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int cus);
 hipError_t launch_gemm_decode(const DecodePlan& plan, const void* q, const float* s, const void* w,
                               const float* ws, void* y, int64_t M, int64_t N, int64_t K, hipStream_t st);
 
-// ---- prefill GEMM (M > kDecodeMaxM): LDS-tiled FP8 MFMA
+// ---- mid-size GEMM (kDecodeMaxM < M <= kMidMaxM): weight streaming, R token groups
+// (above 64 rows the 128 x 128 prefill tiles are faster)
+constexpr int kMidMaxM = 64;
+
+struct MidPlan {
+    int groups;          // R: 16-token groups per weight fragment (2, 4 or 8)
+    int strips_per_wg;   // 1 or 2 strips of 16 output columns per workgroup
+    int64_t strips;      // N / 16
+    int64_t workgroups;  // ceil(strips / strips_per_wg)
+    int64_t kblocks;     // K / 128
+    int waves;           // waves per workgroup = K splits
+};
+
+MidPlan plan_mid(int64_t M, int64_t N, int64_t K, int cus);
+
+hipError_t launch_gemm_mid(const MidPlan& plan, const void* q, const float* s, const void* w, const float* ws,
+                           void* y, int64_t M, int64_t N, int64_t K, hipStream_t st);
+
+// ---- prefill GEMM (M > kMidMaxM): LDS-tiled FP8 MFMA
 hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, const float* ws, void* y,
                                int64_t M, int64_t N, int64_t K, int cus, hipStream_t st);
 

@@ -51,7 +51,7 @@ def check_linear(x, w, what, workspace=None):
     return y
 
 
-SHAPES = [(M, N, K) for M in (1, 2, 5, 8, 9, 16, 17, 33, 100, 128, 129, 255, 256, 257, 300, 513)
+SHAPES = [(M, N, K) for M in (1, 2, 5, 8, 9, 16, 17, 32, 33, 64, 65, 100, 128, 129, 255, 256, 257, 300, 513)
           for (N, K) in ((128, 128), (384, 512), (1024, 1152))]
 
 
@@ -155,6 +155,32 @@ def test_decode_split_counts(waves, monkeypatch):
     monkeypatch.setenv("FP8BS_DECODE_WAVES", str(waves))
     x, w = inputs(5, 384, 2048, seed=50 + waves)
     check_linear(x, w, f"decode waves={waves}")
+
+
+@pytest.mark.parametrize("tile", ["256256", "256128", "128256", "128128"])
+@pytest.mark.parametrize("M", [129, 300])
+def test_prefill_tile_shapes(tile, M, monkeypatch):
+    """Every prefill tile shape, ragged M in the clamped (M < 256) and the moved-back
+    last-tile forms."""
+    monkeypatch.setenv("FP8BS_PREFILL_TILE", tile)
+    x, w = inputs(M, 1024, 1152, seed=90 + M)
+    check_linear(x, w, f"prefill tile {tile}")
+
+
+def test_prefill_default_mid_tile():
+    """M = 1024 on the 7168-wide projection: the default schedule picks 128 x 256 tiles."""
+    x, w = inputs(1024, 7168, 1024, seed=97)
+    check_linear(x, w, "prefill 128x256 default")
+
+
+@pytest.mark.parametrize("M", [17, 40, 64])
+@pytest.mark.parametrize("strips,waves", [("1", "8"), ("2", "8"), ("1", "3"), ("2", "5")])
+def test_mid_schedules(M, strips, waves, monkeypatch):
+    """The mid-size kernel (16 < M <= 64) under every strip count and several split-K degrees."""
+    monkeypatch.setenv("FP8BS_MID_STRIPS", strips)
+    monkeypatch.setenv("FP8BS_MID_WAVES", waves)
+    x, w = inputs(M, 1024, 2176, seed=70 + M)
+    check_linear(x, w, f"mid strips={strips} waves={waves}")
 
 
 def test_subnormal_codes_and_scales():
