@@ -40,13 +40,15 @@ METRIC = "FP8 block-GEMM TFLOP/s (prefill) and GB/s (decode M=1..8), % of roofli
 # used only while these files are unchanged.
 KERNEL_SOURCES = {
     "decode": ["gemm_decode.hip", "launch.h", "device_common.h", "api.hip"],
+    "mid": ["gemm_mid.hip", "launch.h", "device_common.h", "api.hip"],
     "prefill": ["gemm_prefill.hip", "launch.h", "device_common.h", "api.hip"],
 }
-DECODE_MAX_M = 16               # block_linear takes the decode kernel for M <= 16
+DECODE_MAX_M = 16               # block_linear takes the decode kernel for M <= 16,
+MID_MAX_M = 64                  # the mid-size kernel for M <= 64, else the prefill tiles
 
 
 def gemm_kind(M):
-    return "decode" if M <= DECODE_MAX_M else "prefill"
+    return "decode" if M <= DECODE_MAX_M else ("mid" if M <= MID_MAX_M else "prefill")
 
 
 def kernel_source_hash(kind):
@@ -212,6 +214,41 @@ def time_rmsnorm_quant(wl, steps):
     return {"M": M, "K": K, "us": round(us, 2),
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4)}}
+
+
+def time_m_sweep(Ms=(32, 64, 128, 512, 2048), N=7168, K=7168, copies=8, steps=40):
+    """block_linear on the o_proj shape (N = K = 7168) for row counts between the
+    decode and the prefill workloads: batched decode and chunked prefill.  Weights
+    from the prefill_oproj generator, rotated over `copies` copies."""
+    import numpy as np
+    import torch
+    import fp8_block_scaled_amd as fb
+    import synth
+    wl = synth.WORKLOADS["prefill_oproj"]
+    w = torch.from_numpy(synth.make_weight(wl).view(np.int16)).cuda()
+    qw, ws = fb.quant_weight(w)
+    del w
+    sets = [(qw, ws)] + [(qw.clone(), ws.clone()) for _ in range(copies - 1)]
+    out = {}
+    for M in Ms:
+        x = torch.from_numpy(synth.activation_rows(wl, np.arange(M)).view(np.int16)).cuda()
+        q, s = fb.quant_act(x)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        for i in range(3):
+            fb.block_linear(q, s, *sets[i % copies], out=y)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                fb.block_linear(q, s, *sets[i % copies], out=y)
+        graph.replay()
+        us = _replay_ms(graph) * 1e3 / steps
+        nbytes = N * K + 4 * (N // 128) * (K // 128) + M * K + 4 * M * (K // 128) + 2 * M * N
+        out[str(M)] = {"kernel": gemm_kind(M), "us": round(us, 2),
+                       "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                       "TFLOP/s": round(2 * M * N * K / (us * 1e-6) / 1e12, 1)}
+        del graph, x, q, s, y
+    return out
 
 
 def roofline_for(wl, gemm_us, traffic):
@@ -432,6 +469,8 @@ def main():
             del c2
             torch.cuda.empty_cache()
         out["workloads"] = others
+        print("[bench] M sweep", file=sys.stderr, flush=True)
+        out["m_sweep"] = time_m_sweep()
         print("[bench] rmsnorm_quant", file=sys.stderr, flush=True)
         out["rmsnorm_quant"] = {name: time_rmsnorm_quant(WORKLOADS[name], 50 if name == "prefill_oproj" else 200)
                                 for name in ("decode_qkv", "prefill_oproj")}
