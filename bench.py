@@ -410,7 +410,7 @@ def main():
         print(json.dumps({"copy_bytes_read": 512 << 20, "copy_bytes_written": 512 << 20, "copies": 10}))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         return 2
     import numpy as np
