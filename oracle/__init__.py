@@ -10,7 +10,9 @@ What it computes follows the "Nanbeige4.3-33B FP8" model card (ProCreations),
 introduction and section "Recipe and calibration": W8A8 FP8 with E4M3 weights in
 128x128 blocks and dynamic per-token, group-128 activation scales (scheme
 FP8_BLOCK, "standard minmax" weight quantization).  The E4M3 bit format itself is
-the OCP 8-bit Floating Point Specification (OFP8), E4M3 encoding.
+the OCP 8-bit Floating Point Specification (OFP8), E4M3 encoding.  The weight-only
+NVFP4 variant (``nvfp4``) follows the "Nanbeige4.3-33B-NVFP4-A16" model card and the
+E2M1 element format of the OCP Microscaling specification.
 
 Floating point: scales and quotients are float32 (the precision the method fixes
 for them, see ``quant``); dequantization and the matmul are float64 (``linear``).
@@ -22,6 +24,8 @@ Modules
              quantizer, SiLU(gate)*up in float64 rounded once to BF16.
   rmsnorm -- RMSNorm in float64 rounded once to BF16, then the quantizer.
   linear  -- dequantize-and-matmul in float64 and the output tolerance check.
+  nvfp4   -- the NVFP4 weight-only variant: E2M1 codes, E4M3 group-16 scales and a
+             global scale against BF16 activations, in float64.
 
 Parity pins (tests/test_oracle_*.py) tie every function to something other than
 itself: closed-form code values, the torch CPU float8_e4m3fn cast, an independent
@@ -46,4 +50,10 @@ from .linear import (  # noqa: F401
     check_tolerance,
     REL_TOL,
     RMS_TOL,
+)
+from .nvfp4 import (  # noqa: F401
+    e2m1_decode_table,
+    unpack_fp4,
+    dequant_nvfp4,
+    linear_w4a16_ref,
 )

@@ -38,10 +38,14 @@ from .gen import (  # noqa: F401
     TID_GU,
     TID_W_DOWN,
     TID_GAMMA,
+    TID_W4,
+    TID_W4_SCALE,
     f32_to_bf16_bits,
     normal_rows,
     bf16_normal,
+    uniform_bytes,
     choose,
     sample_rows,
 )
 from .workloads import WORKLOADS, Workload, make_activation, make_weight, activation_rows  # noqa: F401
+from .w4a16 import W4A16_WORKLOADS, W4A16Workload, w4a16_activation_rows, w4a16_weight  # noqa: F401

@@ -14,6 +14,8 @@ TID_ROWS = 4
 TID_GU = 5
 TID_W_DOWN = 6
 TID_GAMMA = 7          # RMSNorm weight vector
+TID_W4 = 8             # packed 4-bit weight codes (two per byte)
+TID_W4_SCALE = 9       # 8-bit per-group weight scale codes
 
 
 def _rng(seed, tid, row):
@@ -65,6 +67,24 @@ def bf16_normal(n_rows, n_cols, sigma, seed, tid, rows=None):
     rows = np.arange(n_rows) if rows is None else rows
     scale = np.full(n_cols, np.float32(sigma), dtype=np.float32)
     return f32_to_bf16_bits(normal_rows(rows, n_cols, seed, tid, scale))
+
+
+def uniform_bytes(n_rows, n_cols, lo, hi, seed, tid):
+    """uint8 [n_rows, n_cols], each byte uniform on the integers [lo, hi], seeded per row."""
+    out = np.empty((n_rows, n_cols), dtype=np.uint8)
+
+    def work(a, b):
+        for i in range(a, b):
+            out[i] = _rng(seed, tid, i).integers(lo, hi + 1, size=n_cols, dtype=np.uint8)
+
+    nt = _threads() if n_rows * n_cols >= (1 << 22) else 1
+    step = (n_rows + nt - 1) // nt if n_rows else 1
+    if nt == 1:
+        work(0, n_rows)
+    else:
+        with ThreadPoolExecutor(nt) as ex:
+            list(ex.map(lambda a: work(a, min(n_rows, a + step)), range(0, n_rows, step)))
+    return out
 
 
 def choose(n_total, n_pick, seed, tid):

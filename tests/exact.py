@@ -90,3 +90,19 @@ def nearest_e4m3_code(r, mags, negative):
 
 def np_f32(x):
     return np.float32(x)
+
+
+def minifloat_exact(code, ebits, mbits, bias):
+    """Exact Fraction of a sign/exponent/mantissa code of a binary minifloat with
+    gradual underflow (exponent field 0: m * 2^(1 - bias - mbits)), ignoring any
+    infinity or NaN encodings.  A generic decoder written from the IEEE-style layout,
+    checked against torch's float8 decodes before it is trusted for other formats."""
+    c = int(code)
+    sign = -1 if (c >> (ebits + mbits)) & 1 else 1
+    e = (c >> mbits) & ((1 << ebits) - 1)
+    m = c & ((1 << mbits) - 1)
+    if e == 0:
+        mag = Fraction(m) * Fraction(2) ** (1 - bias - mbits)
+    else:
+        mag = (1 + Fraction(m, 1 << mbits)) * Fraction(2) ** (e - bias)
+    return sign * mag

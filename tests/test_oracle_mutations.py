@@ -7,10 +7,12 @@ import pytest
 import oracle
 import oracle.e4m3 as e4m3
 import oracle.linear as linear
+import oracle.nvfp4 as nvfp4
 import oracle.quant as quant
 import oracle.rmsnorm as rmsnorm
 from tests import test_oracle_e4m3 as te
 from tests import test_oracle_linear as tl
+from tests import test_oracle_nvfp4 as tn
 from tests import test_oracle_quant as tq
 from tests import test_oracle_rmsnorm as tr
 from tests import test_oracle_silu as ts
@@ -101,6 +103,44 @@ def _rmsnorm_variant(sum_not_mean=False, eps_outside=False, round_normalized=Fal
     return f
 
 
+def _unpack_high_first(packed):
+    p = np.asarray(packed, dtype=np.uint8)
+    codes = np.empty((p.shape[0], 2 * p.shape[1]), dtype=np.uint8)
+    codes[:, 0::2] = p >> 4
+    codes[:, 1::2] = p & 0x0F
+    return codes
+
+
+def _e2m1_bias0():
+    t = np.empty(16)
+    for c in range(16):
+        e, m = (c >> 1) & 3, c & 1
+        v = m * 1.0 if e == 0 else (1 + m / 2) * 2.0 ** e
+        t[c] = -v if c & 8 else v
+    return t
+
+
+def _e2m1_subnormal_as_normal():
+    t = nvfp4.e2m1_decode_table().copy()
+    t[1], t[9] = 0.75, -0.75                              # 2^(0-1) * (1 + 1/2)
+    return t
+
+
+def _dequant_nvfp4_variant(divide_g=False, strided=False, no_scale=False):
+    def f(packed, bs, g):
+        codes = nvfp4.unpack_fp4(packed)
+        N, K = codes.shape
+        sc = e4m3.decode(np.asarray(bs, np.uint8))
+        if no_scale:
+            sc = np.ones_like(sc)
+        kk = np.arange(K)
+        grp = (kk % (K // 16)) if strided else kk // 16
+        w = nvfp4._E2M1[codes] * sc[:, grp]
+        gv = float(np.float32(g))
+        return w / gv if divide_g else w * gv
+    return f
+
+
 MUTATIONS = {
     "ties_away_from_zero": ([(e4m3, "encode_rne_sat", _encode_ties_away), (quant, "encode_rne_sat", _encode_ties_away),
                              (oracle, "encode_rne_sat", _encode_ties_away)],
@@ -128,6 +168,18 @@ MUTATIONS = {
     "rmsnorm_double_rounding": ([(rmsnorm, "rmsnorm_bf16", _rmsnorm_variant(round_normalized=True)),
                                  (oracle, "rmsnorm_bf16", _rmsnorm_variant(round_normalized=True))],
                                 [tr.test_rmsnorm_matches_exact_decimal]),
+    "fp4_high_nibble_first": ([(nvfp4, "unpack_fp4", _unpack_high_first), (oracle, "unpack_fp4", _unpack_high_first)],
+                              [tn.test_unpack_nibble_order]),
+    "e2m1_bias_zero": ([(nvfp4, "_E2M1", _e2m1_bias0())],
+                       [tn.test_matches_exact_rational_triple_loop]),
+    "e2m1_subnormal_as_normal": ([(nvfp4, "_E2M1", _e2m1_subnormal_as_normal())],
+                                 [tn.test_matches_exact_rational_triple_loop]),
+    "nvfp4_global_scale_divides": ([(nvfp4, "dequant_nvfp4", _dequant_nvfp4_variant(divide_g=True))],
+                                   [tn.test_matches_exact_rational_triple_loop]),
+    "nvfp4_strided_groups": ([(nvfp4, "dequant_nvfp4", _dequant_nvfp4_variant(strided=True))],
+                             [lambda: tn.test_single_column_spike_picks_its_code_and_group_scale(47)]),
+    "nvfp4_block_scale_dropped": ([(nvfp4, "dequant_nvfp4", _dequant_nvfp4_variant(no_scale=True))],
+                                  [tn.test_matches_exact_rational_triple_loop]),
 }
 
 

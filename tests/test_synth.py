@@ -57,3 +57,27 @@ def test_workload_shapes_and_algorithmic_work():
     assert WORKLOADS["spec_mlp_down"].gemm_bytes() == 58_916_864
     assert WORKLOADS["prefill_oproj"].gemm_flops() == 2 * 8191 * 7168 * 7168
     assert WORKLOADS["tiny"].gemm_bytes() == 201_840
+
+
+def test_w4a16_weights_bytes_and_scale():
+    wl = synth.W4A16_WORKLOADS["w4a16_decode_down"]
+    small = synth.W4A16Workload("probe", 1, wl.K, 64)
+    p, s, g = synth.w4a16_weight(small)
+    assert p.shape == (64, wl.K // 2) and s.shape == (64, wl.K // 16) and g.dtype == np.float32
+    assert s.min() == 0x60 and s.max() == 0x77
+    counts = np.bincount(np.concatenate([p & 15, p >> 4]).ravel(), minlength=16)
+    assert counts.min() > 0.9 * counts.mean()
+    # rows regenerate independently of the tensor's size
+    p2, s2, _ = synth.w4a16_weight(synth.W4A16Workload("probe", 1, wl.K, 8))
+    assert np.array_equal(p2, p[:8]) and np.array_equal(s2, s[:8])
+    import oracle
+    assert abs(oracle.dequant_nvfp4(p, s, g).std() / 0.02 - 1.0) < 0.05
+
+
+def test_w4a16_workload_shapes():
+    W = synth.W4A16_WORKLOADS
+    assert (W["w4a16_decode_qkv"].M, W["w4a16_decode_qkv"].K, W["w4a16_decode_qkv"].N) == (1, 7168, 9216)
+    assert W["w4a16_decode_qkv"].gemm_bytes() == 9216 * 3584 + 9216 * 448 + 2 * 7168 + 2 * 9216
+    assert W["w4a16_prefill_chunk"].gemm_flops() == 2 * 2048 * 7168 * 7168
+    x = synth.w4a16_activation_rows(W["w4a16_decode_qkv"], np.arange(4))
+    assert x.shape == (4, 7168) and x.dtype == np.uint16
