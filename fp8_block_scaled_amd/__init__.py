@@ -10,6 +10,7 @@ outputs and pass raw pointers.
     y = block_linear(q, s, qw, ws)            # y: bf16 [M, N]
     q2, s2 = silu_mul_quant(gu)               # gu: bf16 [M, 2I] -> codes of BF16(silu(g)*u)
     q3, s3 = rmsnorm_quant(x, gamma, 1e-5)    # codes of BF16(RMSNorm(x) * gamma)
+    y4 = nvfp4_linear(x, w4, bs, g)           # NVFP4 weights: w4 uint8 [N, K/2], bs [N, K/16]
 
 Tensor dtypes: BF16 tensors are torch.bfloat16; E4M3 codes are torch.uint8 (view
 them as torch.float8_e4m3fn if wanted); scales are torch.float32.
@@ -25,6 +26,7 @@ __all__ = [
     "silu_mul_quant",
     "rmsnorm_quant",
     "block_linear",
+    "nvfp4_linear",
     "workspace_size",
     "get_workspace",
     "Fp8bsError",
@@ -152,4 +154,23 @@ def block_linear(q, s, qw, ws, out=None, workspace=None):
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _call("fp8_block_linear", dev, q.data_ptr(), s.data_ptr(), qw.data_ptr(), ws.data_ptr(), y.data_ptr(),
           M, N, K, wptr, wbytes)
+    return y
+
+
+def nvfp4_linear(x, w4, bs, g, out=None):
+    """y [M, N] bf16 = x @ W^T, W[n, k] = e2m1(w4 codes) * e4m3(bs[n, k/16]) * g.
+
+    x: bf16 [M, K]; w4: uint8 [N, K/2] packed codes (element 2j in the low nibble of
+    byte j); bs: uint8 (or float8_e4m3fn) [N, K/16] group scales; g: float global scale.
+    """
+    _check_tensor(x, "x", _BF16, 2)
+    _check_tensor(w4, "w4", (torch.uint8,), 2)
+    _check_tensor(bs, "bs", _CODES, 2)
+    M, K = x.shape
+    N = w4.shape[0]
+    if w4.shape[1] * 2 != K or bs.shape != (N, K // 16):
+        raise ValueError("w4 must be [N, K/2] and bs [N, K/16]")
+    dev = x.device
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    _call("nvfp4_w4a16_linear", dev, x.data_ptr(), w4.data_ptr(), bs.data_ptr(), float(g), y.data_ptr(), M, N, K)
     return y

@@ -53,4 +53,23 @@ hipError_t launch_gemm_mid(const MidPlan& plan, const void* q, const float* s, c
 hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, const float* ws, void* y,
                                int64_t M, int64_t N, int64_t K, int cus, hipStream_t st);
 
+// ---- NVFP4 weight-only linear (W4A16): weight streaming, R 16-token groups per
+// dequantized fragment, M covered in chunks of 16 R rows (second grid dimension)
+constexpr int64_t kW4MaxChunks = 65535;   // grid.y limit; larger M is split on the host
+
+struct W4Plan {
+    int groups;          // R: 16-token groups per weight fragment (1, 2 or 4)
+    int strips_per_wg;   // 1 or 2 strips of 16 output columns per workgroup
+    int64_t strips;      // N / 16
+    int64_t strip_wgs;   // ceil(strips / strips_per_wg)
+    int64_t m_chunks;    // ceil(M / (16 R))
+    int64_t kblocks;     // K / 128
+    int waves;           // waves per workgroup = K splits
+};
+
+W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus);
+
+hipError_t launch_w4a16(const W4Plan& plan, const void* x, const void* w, const void* bs, float g, void* y,
+                        int64_t M, int64_t N, int64_t K, hipStream_t st);
+
 }  // namespace fp8bs

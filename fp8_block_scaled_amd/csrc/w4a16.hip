@@ -1,0 +1,252 @@
+// NVFP4 weight-only linear (W4A16) on gfx950: weight-streaming kernel.
+//
+// y[m, n] = g * sum_k x[m, k] * e2m1(code[n, k]) * e4m3(bs[n, k / 16])
+// ("Nanbeige4.3-33B-NVFP4-A16" model card, paragraph on the base revision and
+// calibration: E2M1 weights in groups of 16 with E4M3 group scales and a global
+// scale; BF16 activations).
+//
+// Dequantization is exact and happens in registers: gfx950 converts a byte of two
+// E2M1 codes to two float32 values in one instruction (v_cvt_scalef32_pk_f32_fp4;
+// its scale operand contributes only its exponent, so it is left at 1.0), one
+// multiply applies the group scale (a 2-bit times a 4-bit significand: exact), and
+// v_cvt_pk_bf16_f32 packs the exact products into BF16 pairs.  The products then
+// meet the BF16 activations in v_mfma_f32_16x16x32_bf16, whose FP32 accumulation
+// needs no promotion step (the group scales are already inside the operand); the
+// global scale multiplies once at the end.
+//
+// Decode and batched decode (M up to 64) are bound by the weight stream: 0.5625
+// bytes per weight against 2 M flops.  One workgroup takes NS strips of 16 output
+// columns; its S waves split the 128-wide K blocks, each wave dequantizes a strip's
+// fragment once and multiplies it by R 16-token groups of the activations; partial
+// sums are added through LDS in a fixed order (deterministic).  A second grid
+// dimension covers M in chunks of 16 R rows (rows past M are loaded from row M - 1
+// and not stored).
+//
+// MFMA operands per lane l (g = l / 16, r = l % 16) and K block kb: the lane loads
+// the 16 code bytes [64 kb + 16 g, +16) of weight row 16 st + r, i.e. codes
+// k = 128 kb + 32 g + i, i < 32.  MFMA j (j < 4) takes codes i in [8 j, 8 j + 8)
+// (dword j; group 2 g + j / 2) as B column r, and activations
+// x[m][128 kb + 32 g + 8 j + e], e < 8, of token row m = 16 rho + r as A row r.
+// A and B use the same k for the same (lane group, element), which is all the
+// contraction needs.  Result lane l holds C[4 g + e][r]: token 16 rho + 4 g + e,
+// output column 16 st + r.
+#include <cstdlib>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8bs {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef float v8f __attribute__((ext_vector_type(8)));
+
+constexpr int kW4MaxWaves = 8;
+
+struct W4Args {
+    const uint8_t* w;        // [N, K/2] packed codes
+    const uint8_t* bs;       // [N, K/16] E4M3 group scales
+    const uint16_t* x;       // [M, K] BF16
+    uint16_t* y;             // [M, N] BF16
+    float g;
+    int M;
+    int64_t N, K, KB;
+    int64_t strips;          // N / 16
+};
+
+// Eight weights of one MFMA operand: the codes of dword c (element 2 i in the low
+// nibble of byte i) times the group scale s, as BF16 (exact).
+__device__ __forceinline__ v8bf dequant8(uint32_t c, float s) {
+    const v2f p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+    const v2f p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+    const v2f p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+    const v2f p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+    const v8f v = {p0[0] * s, p0[1] * s, p1[0] * s, p1[1] * s, p2[0] * s, p2[1] * s, p3[0] * s, p3[1] * s};
+    return __builtin_convertvector(v, v8bf);
+}
+
+__device__ __forceinline__ v8bf as_bf8(v4i v) {
+    v8bf r;
+    __builtin_memcpy(&r, &v, sizeof(r));
+    return r;
+}
+
+template <int R, int NS>
+__global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_stream_kernel(W4Args a) {
+    extern __shared__ __attribute__((aligned(16))) v4f red[];      // [S][NS][R][64] partial sums
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = blockDim.x >> 6;
+    const int g = lane >> 4, r = lane & 15;
+    const int64_t strip0 = (int64_t)blockIdx.x * NS;
+    const int m0 = blockIdx.y * 16 * R;
+    const int64_t kb0 = (wave * a.KB) / S;
+    const int64_t kb1 = ((wave + 1) * a.KB) / S;
+
+    const uint16_t* xrow[R];
+#pragma unroll
+    for (int rho = 0; rho < R; ++rho) {
+        const int m = m0 + 16 * rho + r < a.M ? m0 + 16 * rho + r : a.M - 1;
+        xrow[rho] = a.x + (int64_t)m * a.K + 32 * g;
+    }
+    const uint8_t* wrow[NS];
+    const uint8_t* srow[NS];
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+        // Strips past the last one (a partial final workgroup) re-read the last
+        // strip; their results are not stored.
+        const int64_t st = strip0 + q < a.strips ? strip0 + q : a.strips - 1;
+        const int64_t n = st * 16 + r;
+        wrow[q] = a.w + n * (a.K / 2) + 16 * g;
+        srow[q] = a.bs + n * (a.K / 16) + 2 * g;
+    }
+
+    v4f acc[NS][R];
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+#pragma unroll
+        for (int rho = 0; rho < R; ++rho) acc[q][rho] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    struct Frag {
+        v4i wv[NS];
+        uint32_t sv[NS];
+        v4i xv[R][4];
+    };
+    auto load = [&](Frag& f, int64_t kb) {
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+            f.wv[q] = *reinterpret_cast<const v4i*>(wrow[q] + kb * 64);
+            f.sv[q] = *reinterpret_cast<const uint16_t*>(srow[q] + kb * 8);
+        }
+#pragma unroll
+        for (int rho = 0; rho < R; ++rho) {
+            const v4i* xp = reinterpret_cast<const v4i*>(xrow[rho] + kb * kGroup);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f.xv[rho][j] = xp[j];
+        }
+    };
+    auto compute = [&](const Frag& f) {
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+            const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)f.sv[q], 0);
+            const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)f.sv[q], 1);
+            v8bf b[4];
+            b[0] = dequant8((uint32_t)f.wv[q].x, s0);
+            b[1] = dequant8((uint32_t)f.wv[q].y, s0);
+            b[2] = dequant8((uint32_t)f.wv[q].z, s1);
+            b[3] = dequant8((uint32_t)f.wv[q].w, s1);
+#pragma unroll
+            for (int rho = 0; rho < R; ++rho)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[q][rho] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(f.xv[rho][j]), b[j], acc[q][rho], 0, 0, 0);
+        }
+    };
+    // Four token groups hold 64 activation registers per K block: one block in flight.
+    constexpr bool kTwoInFlight = R <= 2;
+    if (!kTwoInFlight) {
+        Frag f;
+        for (int64_t kb = kb0; kb < kb1; ++kb) {
+            load(f, kb);
+            compute(f);
+        }
+    } else if (kb0 < kb1) {
+        Frag fa, fb;
+        load(fa, kb0);
+        int64_t kb = kb0;
+        for (; kb + 1 < kb1; kb += 2) {
+            load(fb, kb + 1);
+            compute(fa);
+            if (kb + 2 < kb1) load(fa, kb + 2);
+            compute(fb);
+        }
+        if (kb < kb1) compute(fa);
+    }
+
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+#pragma unroll
+        for (int rho = 0; rho < R; ++rho) red[((wave * NS + q) * R + rho) * 64 + lane] = acc[q][rho];
+    __syncthreads();
+    // Output o: r = o % 16 fastest (16 neighbouring columns per 16 threads), then
+    // the lane group gg, the element e, and (q, rho).
+    for (int o = threadIdx.x; o < NS * R * 256; o += blockDim.x) {
+        const int rr = o & 15, gg = (o >> 4) & 3, e = (o >> 6) & 3, qr = o >> 8;
+        const int q = qr / R, rho = qr % R;
+        const int m = m0 + 16 * rho + 4 * gg + e;
+        if (m >= a.M || strip0 + q >= a.strips) continue;
+        const int l = gg * 16 + rr;
+        float sum = 0.0f;
+        for (int w = 0; w < S; ++w) sum += red[((w * NS + q) * R + rho) * 64 + l][e];
+        const int64_t n = (strip0 + q) * 16 + rr;
+        a.y[(int64_t)m * a.N + n] = (uint16_t)f32_to_bf16_rne(a.g * sum);
+    }
+}
+
+W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus) {
+    W4Plan p{};
+    p.groups = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    p.strips = N / 16;
+    p.kblocks = K / kGroup;
+    p.m_chunks = M > 0 ? (M + 16 * p.groups - 1) / (16 * p.groups) : 0;
+    p.strips_per_wg = (p.strips >= 4 * (int64_t)cus) ? 2 : 1;
+    if (const char* e = getenv("FP8BS_W4_STRIPS")) {        // tuning hook
+        const int v = atoi(e);
+        if (v == 1 || v == 2) p.strips_per_wg = v;
+    }
+    p.strip_wgs = (p.strips + p.strips_per_wg - 1) / p.strips_per_wg;
+    p.waves = (int)(p.kblocks < kW4MaxWaves ? p.kblocks : kW4MaxWaves);
+    if (const char* e = getenv("FP8BS_W4_WAVES")) {         // tuning hook
+        const int v = atoi(e);
+        if (v >= 1 && v <= kW4MaxWaves) p.waves = v;
+    }
+    return p;
+}
+
+template <int R, int NS>
+static hipError_t launch_w4_rns(dim3 grid, dim3 block, unsigned lds, hipStream_t st, const W4Args& a) {
+    // More than 64 KiB of LDS needs the per-kernel limit raised, up to the CU's 160 KiB.
+    static bool attr_set = false;            // idempotent; a race only repeats the call
+    if (lds > 65536 && !attr_set) {
+        const hipError_t e = hipFuncSetAttribute((const void*)w4a16_stream_kernel<R, NS>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((w4a16_stream_kernel<R, NS>), grid, block, lds, st, a);
+    return hipSuccess;
+}
+
+template <int R>
+static hipError_t launch_w4_r(const W4Plan& plan, dim3 grid, dim3 block, unsigned lds, hipStream_t st,
+                              const W4Args& a) {
+    if (plan.strips_per_wg == 2) return launch_w4_rns<R, 2>(grid, block, lds, st, a);
+    return launch_w4_rns<R, 1>(grid, block, lds, st, a);
+}
+
+hipError_t launch_w4a16(const W4Plan& plan, const void* x, const void* w, const void* bs, float gscale, void* y,
+                        int64_t M, int64_t N, int64_t K, hipStream_t st) {
+    if (plan.strip_wgs == 0 || plan.m_chunks == 0) return hipSuccess;
+    W4Args a;
+    a.w = (const uint8_t*)w;
+    a.bs = (const uint8_t*)bs;
+    a.x = (const uint16_t*)x;
+    a.y = (uint16_t*)y;
+    a.g = gscale;
+    a.M = (int)M;
+    a.N = N;
+    a.K = K;
+    a.KB = plan.kblocks;
+    a.strips = plan.strips;
+    const dim3 grid((unsigned)plan.strip_wgs, (unsigned)plan.m_chunks), block(plan.waves * 64);
+    const unsigned lds = (unsigned)(plan.waves * plan.strips_per_wg * plan.groups * 64 * sizeof(v4f));
+    hipError_t e;
+    switch (plan.groups) {
+        case 1: e = launch_w4_r<1>(plan, grid, block, lds, st, a); break;
+        case 2: e = launch_w4_r<2>(plan, grid, block, lds, st, a); break;
+        default: e = launch_w4_r<4>(plan, grid, block, lds, st, a); break;
+    }
+    return e != hipSuccess ? e : hipGetLastError();
+}
+
+}  // namespace fp8bs

@@ -44,7 +44,7 @@ typedef enum {
     FP8BS_ERR_DEVICE = -4,    /* the current device is not gfx950                 */
     FP8BS_ERR_HIP = -5,       /* a HIP runtime call or a kernel launch failed     */
     FP8BS_ERR_WORKSPACE = -6, /* workspace given but misaligned                   */
-    FP8BS_ERR_VALUE = -7      /* a scalar argument out of range (eps <= 0, NaN)   */
+    FP8BS_ERR_VALUE = -7      /* a scalar argument out of range (eps <= 0, NaN g) */
 } fp8bs_status;
 
 /*
@@ -128,13 +128,39 @@ int fp8_block_linear(const void* q_e4m3, const float* s_f32,
  * shapes as well). */
 size_t fp8_block_linear_workspace_size(int64_t M, int64_t N, int64_t K);
 
+/*
+ * NVFP4 weight-only linear (W4A16): y = x @ W^T with BF16 activations and
+ *   W[n, k] = e2m1(code[n, k]) * e4m3(bs[n, k/16]) * g.
+ * The scheme of the "Nanbeige4.3-33B-NVFP4-A16" model card (paragraph on the base
+ * revision and calibration): FP4 E2M1 weights in groups of 16 along K, an E4M3
+ * scale per group and a global weight scale; activations are not quantized.  The
+ * card's serving layout keeps packed FP4 values and block scales and stores the
+ * global scale as a multiplier.
+ *   x_bf16   [M, K]     BF16 activations (in).
+ *   w_fp4    [N, K/2]   packed codes (in): byte j of row n holds element 2j in bits
+ *                       0-3 and element 2j+1 in bits 4-7.  A code is OCP MX E2M1 (sign,
+ *                       2 exponent bits with bias 1, 1 mantissa bit: +-{0, 0.5, 1, 1.5,
+ *                       2, 3, 4, 6}).
+ *   bs_e4m3  [N, K/16]  group scales (in), OCP E4M3 bytes; the NaN codes 0x7F / 0xFF
+ *                       are outside the contract.
+ *   g                   global scale, any finite float32 (else FP8BS_ERR_VALUE).
+ *   y_bf16   [M, N]     output (out): fl32(g * acc) rounded to BF16 (nearest even).
+ * Shapes follow the shared rule (K and N multiples of 128).  Alignment: x, w, y and
+ * bs 16-byte aligned.  Each product e2m1 * e4m3 is exact in BF16 and each product
+ * with x exact in FP32; acc is their FP32 sum in an order fixed for a given
+ * (M, N, K, device), so repeated calls give bitwise-identical outputs.  Accuracy:
+ * |y - ref| <= 4e-3 |ref| + 1e-3 rms(ref) against the exact dequantize-and-matmul.
+ */
+int nvfp4_w4a16_linear(const void* x_bf16, const void* w_fp4, const void* bs_e4m3, float g,
+                       void* y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char* fp8bs_status_string(int status);
 
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int fp8bs_abi_version(void);
 
-#define FP8BS_ABI_VERSION 10100
+#define FP8BS_ABI_VERSION 10200
 
 #ifdef __cplusplus
 }

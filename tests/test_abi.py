@@ -20,7 +20,7 @@ A16, A16b, A16c, A16d, A16e = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s*(fp8\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s*((?:fp8|nvfp4)\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +30,7 @@ def L():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert {"fp8_quant_act", "fp8_block_linear"} <= set(names)
+    assert {"fp8_quant_act", "fp8_block_linear", "nvfp4_w4a16_linear"} <= set(names)
     assert set(names) == set(_lib.SIGNATURES), names
 
 
@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8bs_abi_version() == 10100
+    assert L.fp8bs_abi_version() == 10200
     for st in (OK, ENULL, ESHAPE, EALIGN, EDEV, EHIP, EWS, EVAL):
         assert L.fp8bs_status_string(st)
     assert b"unknown" in L.fp8bs_status_string(12345)
@@ -92,6 +92,25 @@ def test_block_linear_validation(L):
     assert f(A16, A16b, A16c, A16d, A16e, 4, 128, 128, A16 + 16, 4096, None) == EWS
     assert f(None, None, None, None, None, 0, 128, 128, None, 0, None) == OK     # M == 0
     assert f(None, None, None, None, None, 4, 0, 128, None, 0, None) == OK       # N == 0
+
+
+def test_nvfp4_linear_validation(L):
+    f = L.nvfp4_w4a16_linear
+    assert f(A16, A16b, A16c, 1.0, A16d, 4, 100, 128, None) == ESHAPE
+    assert f(A16, A16b, A16c, 1.0, A16d, 4, 128, 112, None) == ESHAPE
+    assert f(A16, A16b, A16c, 1.0, A16d, 4, 128, 0, None) == ESHAPE
+    assert f(A16, A16b, A16c, 1.0, A16d, -1, 128, 128, None) == ESHAPE
+    assert f(A16, A16b, A16c, 1.0, A16d, 1 << 32, 128, 128, None) == ESHAPE     # 32-bit token rows
+    assert f(A16, A16b, A16c, float("nan"), A16d, 4, 128, 128, None) == EVAL
+    assert f(A16, A16b, A16c, float("inf"), A16d, 4, 128, 128, None) == EVAL
+    assert f(None, A16b, A16c, 1.0, A16d, 4, 128, 128, None) == ENULL
+    assert f(A16, A16b, None, 1.0, A16d, 4, 128, 128, None) == ENULL
+    assert f(A16 + 2, A16b, A16c, 1.0, A16d, 4, 128, 128, None) == EALIGN
+    assert f(A16, A16b + 8, A16c, 1.0, A16d, 4, 128, 128, None) == EALIGN
+    assert f(A16, A16b, A16c + 8, 1.0, A16d, 4, 128, 128, None) == EALIGN
+    assert f(A16, A16b, A16c, 1.0, A16d + 2, 4, 128, 128, None) == EALIGN
+    assert f(None, None, None, 1.0, None, 0, 128, 128, None) == OK          # M == 0
+    assert f(None, None, None, -2.5, None, 4, 0, 128, None) == OK           # N == 0
 
 
 def test_valid_call_without_a_gpu_reports_a_hip_error_not_a_crash(L):

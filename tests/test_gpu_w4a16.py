@@ -1,0 +1,140 @@
+"""GPU parity: the HIP NVFP4 weight-only linear against the float64 oracle.
+
+Every element must satisfy |y - ref| <= 4e-3 |ref| + 1e-3 rms(ref).  Cases whose
+result is exactly representable (one-hot activations with g = 1 read back single
+dequantized weights) are compared bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_amd as fb
+import oracle
+import synth
+from tests.gpu_util import assert_bits_equal, banner, dev_bf16, dev_u8, host_u16
+
+pytestmark = pytest.mark.gpu
+
+# E4M3 codes without the two NaN patterns.
+E4M3_FINITE = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+
+
+def bf16(x):
+    x = np.asarray(x, dtype=np.float32)
+    return synth.f32_to_bf16_bits(x).reshape(x.shape)
+
+
+def random_case(M, N, K, seed, scale_codes=None):
+    rng = np.random.default_rng(seed)
+    x = bf16(rng.standard_normal((M, K)))
+    w4 = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    if scale_codes is None:
+        bs = rng.integers(0x30, 0x78, size=(N, K // 16), dtype=np.uint8)
+    else:
+        bs = rng.choice(scale_codes, size=(N, K // 16)).astype(np.uint8)
+    return x, w4, bs
+
+
+def gpu(x, w4, bs, g):
+    y = fb.nvfp4_linear(dev_bf16(x), dev_u8(w4), dev_u8(bs), g)
+    torch.cuda.synchronize()
+    return host_u16(y)
+
+
+def check(x, w4, bs, g, what):
+    banner(f"nvfp4_linear {what} M={x.shape[0]} N={w4.shape[0]} K={x.shape[1]}")
+    y = gpu(x, w4, bs, g)
+    res = oracle.check_tolerance(y, oracle.linear_w4a16_ref(x, w4, bs, g))
+    assert res["ok"], f"{what}: {res}"
+    return y
+
+
+SHAPES = [(M, N, K) for M in (1, 2, 5, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 128, 129, 300)
+          for (N, K) in ((128, 128), (384, 512), (1024, 1152))]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_shapes(M, N, K):
+    x, w4, bs = random_case(M, N, K, seed=M * 131 + N + K)
+    check(x, w4, bs, np.float32(3.7e-3), "random")
+
+
+@pytest.mark.parametrize("M", [1, 16, 40, 200])
+def test_every_scale_code(M):
+    """Scales drawn from every finite E4M3 code: zero, subnormal, negative, 448."""
+    x, w4, bs = random_case(M, 512, 1024, seed=900 + M, scale_codes=E4M3_FINITE)
+    check(x, w4, bs, np.float32(0.75), "every scale code")
+
+
+def test_dequantized_weights_bitwise():
+    """x = identity (128 tokens x 128 channels), g = 1: y = W^T exactly, for every
+    code in every group position and every finite scale code."""
+    N, K = 512, 128
+    rng = np.random.default_rng(77)
+    w4 = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    bs = np.resize(E4M3_FINITE, N * (K // 16)).reshape(N, K // 16)
+    x = bf16(np.eye(K, dtype=np.float32))
+    banner("nvfp4_linear identity activations bitwise")
+    y = gpu(x, w4, bs, np.float32(1.0))
+    want = oracle.dequant_nvfp4(w4, bs, np.float32(1.0)).T                  # exact in BF16
+    want_bits = bf16(want.astype(np.float32))
+    got = y.copy()
+    got[(got & 0x7FFF) == 0] = 0                                           # +-0 both fine
+    want_bits[(want_bits & 0x7FFF) == 0] = 0
+    assert_bits_equal(got, want_bits, "identity readback")
+
+
+@pytest.mark.parametrize("k", [0, 1, 15, 16, 31, 32, 63, 64, 127, 128, 255])
+def test_one_hot_decode_row(k):
+    """M = 1 with x one-hot at column k reads back column k of W (decode path)."""
+    N, K = 256, 256
+    rng = np.random.default_rng(k)
+    w4 = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    bs = rng.choice(E4M3_FINITE, size=(N, K // 16)).astype(np.uint8)
+    x = np.zeros((1, K), np.float32)
+    x[0, k] = 1.0
+    banner(f"nvfp4_linear one-hot k={k}")
+    y = gpu(bf16(x), w4, bs, np.float32(1.0))
+    want = bf16(oracle.dequant_nvfp4(w4, bs, np.float32(1.0))[:, k].astype(np.float32))[None, :]
+    y[(y & 0x7FFF) == 0] = 0
+    want[(want & 0x7FFF) == 0] = 0
+    assert_bits_equal(y, want, f"one-hot column {k}")
+
+
+def test_global_scale_sign_and_zero():
+    x, w4, bs = random_case(24, 384, 512, seed=5)
+    y1 = gpu(x, w4, bs, np.float32(0.5))
+    yn = gpu(x, w4, bs, np.float32(-0.5))
+    assert_bits_equal(yn ^ np.uint16(0x8000), y1, "negated global scale")
+    y0 = gpu(x, w4, bs, np.float32(0.0))
+    assert not np.any(y0 & 0x7FFF)
+
+
+@pytest.mark.parametrize("M", [1, 8, 50, 300])
+def test_deterministic(M):
+    x, w4, bs = random_case(M, 1024, 2048, seed=M + 3)
+    banner(f"nvfp4_linear repeat M={M}")
+    assert_bits_equal(gpu(x, w4, bs, np.float32(1e-2)), gpu(x, w4, bs, np.float32(1e-2)), "repeat")
+
+
+def test_empty_and_errors():
+    e = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    w4 = torch.zeros((128, 128), dtype=torch.uint8, device="cuda")
+    bs = torch.zeros((128, 16), dtype=torch.uint8, device="cuda")
+    assert fb.nvfp4_linear(e, w4, bs, 1.0).shape == (0, 128)
+    x = torch.zeros((4, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fb.Fp8bsError):
+        fb.nvfp4_linear(x, w4, bs, float("nan"))
+
+
+@pytest.mark.parametrize("name", sorted(synth.W4A16_WORKLOADS))
+def test_workload(name):
+    wl = synth.W4A16_WORKLOADS[name]
+    w4, bs, g = synth.w4a16_weight(wl)
+    x = synth.w4a16_activation_rows(wl, np.arange(wl.M))
+    banner(f"nvfp4_linear workload {name} M={wl.M} N={wl.N} K={wl.K}")
+    y = gpu(x, w4, bs, g)
+    rows = synth.sample_rows(wl.M, wl.sampled_rows, wl.seed) if wl.sampled_rows else np.arange(wl.M)
+    ref = oracle.linear_w4a16_ref(x[rows], w4, bs, g)
+    res = oracle.check_tolerance(y[rows], ref)
+    assert res["ok"], f"{name}: {res}"
