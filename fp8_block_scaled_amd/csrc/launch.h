@@ -65,6 +65,11 @@ struct W4Plan {
     int64_t m_chunks;    // ceil(M / (16 R))
     int64_t kblocks;     // K / 128
     int waves;           // waves per workgroup = K splits
+    int decode_p;        // > 0: decode kernel (M <= 16) with strips of P columns
+    int decode_kbw;      //   super blocks (16 / P K blocks each) per wave
+    int decode_slots;    //   LDS partial-sum slots per wave (>= strips per workgroup)
+    int64_t decode_strips_per_wg;
+    int64_t decode_wgs;
 };
 
 W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus);

@@ -101,6 +101,31 @@ def test_one_hot_decode_row(k):
     assert_bits_equal(y, want, f"one-hot column {k}")
 
 
+DECODE_CASES = [
+    # (M, K, N, env): token groups P = 4 / 8 / 16 with 1, 2, 4 or 8 super blocks per wave
+    (1, 512, 384, None), (3, 2048, 1024, None), (4, 16384, 512, None), (2, 7168, 2048, None),
+    (5, 1024, 384, None), (8, 7168, 1024, None), (6, 4096, 2048, None), (7, 32768, 256, None),
+    (12, 1024, 1024, None), (16, 2048, 384, None), (16, 512, 2048, None), (9, 8192, 1024, None),
+    # K that does not split into equal slices: the streaming kernel
+    (1, 8576, 2048, None), (16, 8576, 1024, None),
+    (1, 7168, 2048, {"FP8BS_W4_DECODE": "0"}), (5, 1152, 1024, {"FP8BS_W4_DECODE": "0"}),
+    # strips per workgroup with ragged tails
+    (1, 7168, 2048, {"FP8BS_W4_DECODE_SPW": "5"}), (8, 8192, 2048, {"FP8BS_W4_DECODE_SPW": "7"}),
+    (2, 2048, 1024, {"FP8BS_W4_DECODE_SPW": "1"}), (3, 1024, 1152, {"FP8BS_W4_DECODE_SPW": "3"}),
+    (16, 512, 1024, {"FP8BS_W4_DECODE_SPW": "9"}),
+]
+
+
+@pytest.mark.parametrize("M,K,N,env", DECODE_CASES)
+def test_decode_schedules(M, K, N, env, monkeypatch):
+    """Every decode schedule (K chunks folded into the MFMA, or streamed) and strip
+    counts with ragged tails give the oracle's result."""
+    for k, v in (env or {}).items():
+        monkeypatch.setenv(k, v)
+    x, w4, bs = random_case(M, N, K, seed=M + K + N)
+    check(x, w4, bs, np.float32(2.0e-3), f"schedule {env}")
+
+
 def test_global_scale_sign_and_zero():
     x, w4, bs = random_case(24, 384, 512, seed=5)
     y1 = gpu(x, w4, bs, np.float32(0.5))
