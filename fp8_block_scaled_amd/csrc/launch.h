@@ -66,9 +66,8 @@ struct W4Plan {
     int64_t kblocks;     // K / 128
     int waves;           // waves per workgroup = K splits
     int decode_p;        // > 0: decode kernel (M <= 16) with strips of P columns
-    int decode_kbw;      //   super blocks (16 / P K blocks each) per wave
-    int decode_slots;    //   LDS partial-sum slots per wave (>= strips per workgroup)
-    int64_t decode_strips_per_wg;
+    int decode_ns;       //   strips per workgroup (1, 2 or 4)
+    int decode_ch;       //   super blocks per load batch (1 or 2)
     int64_t decode_wgs;
 };
 

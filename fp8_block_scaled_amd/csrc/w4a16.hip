@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_stream_kernel(W4Args a
     }
 }
 
-// Decode (M <= 16): K chunks folded into the MFMA, activations held in registers.
+// Decode (M <= 16): K chunks folded into the MFMA.
 //
 // v_mfma_f32_16x16x32_bf16 multiplies 16 rows of A by 16 columns of B over 32
 // k.  With M <= P (P = 4, 8 or 16) the 16 rows and columns are split into
@@ -196,145 +196,112 @@ __global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_stream_kernel(W4Args a
 //
 // k of (MFMA u < 4, group t, lane group g, element e) = 128 t + 32 g + 8 u + e
 // within the super block: lane l (g = l / 16, r = l % 16, t = r / P) loads 16
-// contiguous code bytes of weight row r % P of the strip, its 2 group scales, and
-// (once) 64 contiguous activation bytes of token row r % P (zero when >= M).  A
-// and B use the same k for the same (t, lane group, element), which is all the
-// contraction needs.  Result lane l holds C[4 g + e][r]: token (4 g + e) % P of
-// group (4 g + e) / P against weight row r % P of group r / P; it is a diagonal
-// element when the two groups agree.
+// contiguous code bytes of weight row r % P of the strip and their 2 group scales,
+// and 64 contiguous activation bytes of token row r % P (zeroed at use when the row
+// is >= M or the chunk is past K).  A and B use the same k for the same (t, lane
+// group, element), which is all the contraction needs.  Result lane l holds
+// C[4 g + e][r]: token (4 g + e) % P of group (4 g + e) / P against weight row
+// r % P of group r / P; it is a diagonal element when the two groups agree.  The
+// MFMA accumulates straight into the strip's FP32 sums: the group scales are
+// already inside the dequantized operand, so no promotion step is needed.
 //
-// A workgroup's S waves split the super blocks into equal slices of KBW; each
-// wave loads its activation slice once (16 VGPRs per super block), then streams the
-// workgroup's strips through it with D strips of loads in flight (one 16-byte code
-// load and one 2-byte scale load per lane and super block).  The strip loop has no
-// branches: strip indices past the workgroup's last strip are clamped to it (a
-// repeated load that hits in L2) and their partial sums land in LDS slots that are
-// never read.  The diagonal lanes store their partial sums compactly in LDS; after
-// one barrier every output adds its G chunk groups and S waves in a fixed order.
-constexpr int kW4DecodeMaxWaves = 16;
-constexpr int64_t kW4DecodeSlotBytes = 96 * 1024;   // LDS for partial sums (at most)
-
-template <int P, int KBW>
-struct W4DecodeShape {
-    static constexpr int G = 16 / P;             // chunk groups per MFMA
-    static constexpr int U = 4 * P;              // diagonal lanes per wave
-    static constexpr int D = KBW <= 2 ? 4 : 2;   // strips of loads in flight
-};
-
-// Threads per workgroup at most (the register budget of a wave's slice).
-constexpr int w4_decode_threads(int p, int kbw) {
-    return (kbw == 1 && p == 16 ? 8 : (kbw <= 2 ? 16 : (kbw <= 4 ? 8 : 4))) * 64;
-}
-
-template <int P, int KBW>
-__global__ __launch_bounds__(w4_decode_threads(P, KBW)) void w4a16_decode_kernel(
-    W4Args a, int64_t strips_per_wg, int slots) {
-    typedef W4DecodeShape<P, KBW> Sh;
-    constexpr int G = Sh::G, U = Sh::U, D = Sh::D;
-    extern __shared__ __attribute__((aligned(16))) v4f red[];      // [S][slots][U]
+// One workgroup owns NS adjacent strips; its S waves take equal contiguous ranges
+// of super blocks and each requests the fragments of CH super blocks at a time
+// (branch-free: chunks past K are clamped to valid addresses and zeroed at use).
+// The waves are light on registers, so a CU holds several workgroups and many
+// loads in flight.  Partial sums over waves and groups are added through LDS in a
+// fixed order (deterministic).
+template <int P, int NS, int CH>
+__global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_decode_kernel(W4Args a) {
+    constexpr int G = 16 / P;
+    extern __shared__ __attribute__((aligned(16))) v4f red[];      // [S][NS][64]
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = blockDim.x >> 6;
     const int g = lane >> 4, r = lane & 15;
     const int t = r / P, j = r % P;
-    const int64_t sbk = (int64_t)G * kGroup;                        // k per super block
-    const int64_t k0 = (int64_t)wave * KBW * sbk + 128 * t + 32 * g;   // this lane's first k
-    const int64_t st_begin = (int64_t)blockIdx.x * strips_per_wg;
-    const int64_t st_end = st_begin + strips_per_wg < a.strips ? st_begin + strips_per_wg : a.strips;
-    const int64_t last = st_end - 1;         // >= st_begin: the grid has no empty workgroup
-
-    v4i xv[KBW][4];
+    const bool mvalid = j < a.M;
+    const int64_t strip0 = (int64_t)blockIdx.x * NS;
+    const int64_t SB = (a.KB + G - 1) / G;
+    const int64_t sb0 = (wave * SB) / S;
+    const int64_t sb1 = ((wave + 1) * SB) / S;
+    const uint16_t* xrow = a.x + (int64_t)(mvalid ? j : 0) * a.K + 32 * g;
+    const uint8_t* wrow[NS];
+    const uint8_t* srow[NS];
 #pragma unroll
-    for (int i = 0; i < KBW; ++i)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) xv[i][u] = v4i{0, 0, 0, 0};
-    if (j < a.M) {
-        const uint16_t* xp = a.x + (int64_t)j * a.K + k0;
-#pragma unroll
-        for (int i = 0; i < KBW; ++i)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) xv[i][u] = *reinterpret_cast<const v4i*>(xp + i * sbk + 8 * u);
+    for (int q = 0; q < NS; ++q) {
+        // Strips past the last one (a partial final workgroup) re-read the last
+        // strip; their results are not stored.
+        const int64_t st = strip0 + q < a.strips ? strip0 + q : a.strips - 1;
+        const int64_t n = st * P + j;
+        wrow[q] = a.w + n * (a.K / 2) + 16 * g;
+        srow[q] = a.bs + n * (a.K / 16) + 2 * g;
     }
 
-    struct Frag {
-        v4i wv[KBW];
-        uint32_t sv[KBW];
-    };
-    auto load = [&](Frag& f, int64_t st) {
-        const int64_t n = (st < last ? st : last) * P + j;
-        const uint8_t* wp = a.w + n * (a.K / 2) + k0 / 2;
-        const uint8_t* sp = a.bs + n * (a.K / 16) + k0 / 16;
+    v4i wv[CH][NS], xv[CH][4];
+    uint32_t sv[CH][NS];
+    auto load_batch = [&](int64_t sb) {
 #pragma unroll
-        for (int i = 0; i < KBW; ++i) {
-            f.wv[i] = *reinterpret_cast<const v4i*>(wp + i * (sbk / 2));
-            f.sv[i] = *reinterpret_cast<const uint16_t*>(sp + i * (sbk / 16));
-        }
-    };
-    // A diagonal lane (group of its A rows == group of its column) stores its four
-    // values at compact index g * P + j.
-    const bool diag = (4 * g) / P == t;
-    const int cidx = g * P + j;
-    auto compute_store = [&](const Frag& f, int slot) {
-        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = 0; i < CH; ++i) {
+            int64_t kc = (sb + i) * G + t;                       // K block of this lane's chunk
+            kc = kc < a.KB ? kc : a.KB - 1;
+            const v4i* xp = reinterpret_cast<const v4i*>(xrow + kc * kGroup);
 #pragma unroll
-        for (int i = 0; i < KBW; ++i) {
-            const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)f.sv[i], 0);
-            const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)f.sv[i], 1);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(xv[i][0]), dequant8((uint32_t)f.wv[i].x, s0), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(xv[i][1]), dequant8((uint32_t)f.wv[i].y, s0), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(xv[i][2]), dequant8((uint32_t)f.wv[i].z, s1), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(xv[i][3]), dequant8((uint32_t)f.wv[i].w, s1), acc, 0, 0, 0);
-        }
-        if (diag) red[((int64_t)wave * slots + slot) * U + cidx] = acc;
-    };
-
-    // slots is a multiple of D and >= the workgroup's strip count.
-    Frag fr[D];
+            for (int u = 0; u < 4; ++u) xv[i][u] = xp[u];
 #pragma unroll
-    for (int d = 0; d < D - 1; ++d) load(fr[d], st_begin + d);
-    for (int i = 0; i < slots; i += D) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            load(fr[(d + D - 1) % D], st_begin + i + d + D - 1);
-            compute_store(fr[d], i + d);
-        }
-    }
-    __syncthreads();
-    // Output o: weight row jj fastest (P neighbouring columns), then token, strip.
-    // Token ti of chunk group tt sits at A row P tt + ti = 4 gg + e.
-    const int nb = (int)(st_end - st_begin);
-    for (int o = threadIdx.x; o < nb * P * P; o += blockDim.x) {
-        const int jj = o % P, ti = (o / P) % P, b = o / (P * P);
-        if (ti >= a.M) continue;
-        float sum = 0.0f;
-        for (int w = 0; w < S; ++w)
-            for (int tt = 0; tt < G; ++tt) {
-                const int row = P * tt + ti, gg = row >> 2, e = row & 3;
-                sum += red[((int64_t)w * slots + b) * U + gg * P + jj][e];
+            for (int q = 0; q < NS; ++q) {
+                wv[i][q] = *reinterpret_cast<const v4i*>(wrow[q] + kc * 64);
+                sv[i][q] = *reinterpret_cast<const uint16_t*>(srow[q] + kc * 8);
             }
-        a.y[(int64_t)ti * a.N + (st_begin + b) * P + jj] = (uint16_t)f32_to_bf16_rne(a.g * sum);
-    }
-}
-
-// Decode schedule: P from M; waves S (<= 16) and super blocks per wave KBW
-// (1, 2, 4 or 8) with S * KBW = K / (128 G), preferring the most waves the
-// register budget of the slice allows.  false if K does not split that way.
-static bool decode_shape(int64_t M, int64_t K, int* P, int* S, int* KBW) {
-    *P = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
-    const int64_t G = 16 / *P;
-    if (K % (kGroup * G) != 0) return false;
-    const int64_t SB = K / (kGroup * G);
-    const int kbws[4] = {1, 2, 4, 8};
-    int best_s = 0, best_k = 0;
-    for (int q = 0; q < 4; ++q)
-        if (SB % kbws[q] == 0 && SB / kbws[q] <= w4_decode_threads(*P, kbws[q]) / 64 && SB / kbws[q] > best_s) {
-            best_s = (int)(SB / kbws[q]);
-            best_k = kbws[q];
         }
-    if (best_s == 0) return false;
-    *S = best_s;
-    *KBW = best_k;
-    return true;
+    };
+
+    v4f acc[NS];
+#pragma unroll
+    for (int q = 0; q < NS; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    const v4i z4 = {0, 0, 0, 0};
+    for (int64_t sb = sb0; sb < sb1; sb += CH) {
+        load_batch(sb);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            if (sb + i < sb1) {                                  // uniform
+                const bool use = mvalid && (sb + i) * G + t < a.KB;
+                v8bf xa[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) xa[u] = as_bf8(use ? xv[i][u] : z4);
+#pragma unroll
+                for (int q = 0; q < NS; ++q) {
+                    const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sv[i][q], 0);
+                    const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)sv[i][q], 1);
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0], dequant8((uint32_t)wv[i][q].x, s0), acc[q], 0, 0, 0);
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[1], dequant8((uint32_t)wv[i][q].y, s0), acc[q], 0, 0, 0);
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[2], dequant8((uint32_t)wv[i][q].z, s1), acc[q], 0, 0, 0);
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[3], dequant8((uint32_t)wv[i][q].w, s1), acc[q], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int q = 0; q < NS; ++q) red[(wave * NS + q) * 64 + lane] = acc[q];
+    __syncthreads();
+    // Output (token m, column c) of strip q: sum over waves, then over the G groups,
+    // of the diagonal-block entry C[tt P + m][tt P + c], held by lane
+    // 16 ((tt P + m) / 4) + tt P + c in its component (tt P + m) % 4.
+    for (int o = threadIdx.x; o < NS * a.M * P; o += blockDim.x) {
+        const int q = o / (a.M * P), rem = o % (a.M * P);
+        const int m = rem / P, c = rem % P;
+        if (strip0 + q >= a.strips) continue;
+        float sum = 0.0f;
+        for (int w = 0; w < S; ++w) {
+#pragma unroll
+            for (int tt = 0; tt < G; ++tt) {
+                const int row = tt * P + m;
+                sum += red[(w * NS + q) * 64 + 16 * (row >> 2) + tt * P + c][row & 3];
+            }
+        }
+        a.y[(int64_t)m * a.N + (strip0 + q) * P + c] = (uint16_t)f32_to_bf16_rne(a.g * sum);
+    }
 }
 
 W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus) {
@@ -354,55 +321,47 @@ W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus) {
         const int v = atoi(e);
         if (v >= 1 && v <= kW4MaxWaves) p.waves = v;
     }
-    // Decode: K chunks folded into the MFMA, activations in registers.
-    int P = 0, S = 0, KBW = 0;
+    // Decode: K chunks folded into the MFMA; NS strips of P columns per workgroup.
     const char* de = getenv("FP8BS_W4_DECODE");              // tuning hook: 0 = stream kernel
-    if (M <= 16 && decode_shape(M, K, &P, &S, &KBW) && !(de && atoi(de) == 0)) {
+    if (M <= 16 && !(de && atoi(de) == 0)) {
+        const int P = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
         p.decode_p = P;
-        p.decode_kbw = KBW;
-        p.waves = S;
-        const int Dp = KBW <= 2 ? 4 : 2;
         const int64_t strips = N / P;
-        int64_t spw = (strips + cus - 1) / cus;
-        if (const char* e = getenv("FP8BS_W4_DECODE_SPW")) {  // tuning hook
+        p.decode_ns = strips >= 8 * (int64_t)cus ? 4 : 2;
+        if (const char* e = getenv("FP8BS_W4_DECODE_NS")) {   // tuning hook
             const int v = atoi(e);
-            if (v >= 1) spw = v;
+            if (v == 1 || v == 2 || v == 4) p.decode_ns = v;
         }
-        // LDS: S waves x slots x 4P lanes x 16 bytes.
-        const int64_t per_slot = (int64_t)S * 4 * P * 16;
-        int64_t max_slots = (kW4DecodeSlotBytes / per_slot) / Dp * Dp;
-        if (max_slots < Dp) max_slots = Dp;
-        if (spw > max_slots) spw = max_slots;
-        p.decode_strips_per_wg = spw;
-        p.decode_slots = (int)((spw + Dp - 1) / Dp * Dp);
-        p.decode_wgs = (strips + spw - 1) / spw;              // every workgroup gets a strip
+        p.decode_ch = p.decode_ns <= 2 ? 2 : 1;
+        if (const char* e = getenv("FP8BS_W4_DECODE_CH")) {   // tuning hook
+            const int v = atoi(e);
+            if (v == 1 || v == 2) p.decode_ch = v;
+        }
+        const int64_t SB = (p.kblocks + 16 / P - 1) / (16 / P);
+        p.waves = (int)(SB < kW4MaxWaves ? SB : kW4MaxWaves);
+        if (const char* e = getenv("FP8BS_W4_DECODE_WAVES")) {   // tuning hook
+            const int v = atoi(e);
+            if (v >= 1 && v <= kW4MaxWaves && v <= SB) p.waves = v;
+        }
+        p.decode_wgs = (strips + p.decode_ns - 1) / p.decode_ns;
     }
     return p;
 }
 
-template <int P, int KBW>
+template <int P, int NS, int CH>
 static hipError_t launch_w4_decode(const W4Plan& plan, hipStream_t st, const W4Args& a) {
-    const unsigned lds = (unsigned)((int64_t)plan.waves * plan.decode_slots * 4 * P * sizeof(v4f));
-    static bool attr_set = false;            // idempotent; a race only repeats the call
-    if (lds > 65536 && !attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)w4a16_decode_kernel<P, KBW>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    hipLaunchKernelGGL((w4a16_decode_kernel<P, KBW>), dim3((unsigned)plan.decode_wgs), dim3(plan.waves * 64), lds, st,
-                       a, plan.decode_strips_per_wg, plan.decode_slots);
+    const unsigned lds = (unsigned)(plan.waves * NS * 64 * sizeof(v4f));
+    hipLaunchKernelGGL((w4a16_decode_kernel<P, NS, CH>), dim3((unsigned)plan.decode_wgs), dim3(plan.waves * 64), lds, st,
+                       a);
     return hipGetLastError();
 }
 
 template <int P>
 static hipError_t launch_w4_decode_p(const W4Plan& plan, hipStream_t st, const W4Args& a) {
-    switch (plan.decode_kbw) {
-        case 1: return launch_w4_decode<P, 1>(plan, st, a);
-        case 2: return launch_w4_decode<P, 2>(plan, st, a);
-        case 4: return launch_w4_decode<P, 4>(plan, st, a);
-        default: return launch_w4_decode<P, 8>(plan, st, a);
-    }
+    if (plan.decode_ns == 4) return launch_w4_decode<P, 4, 1>(plan, st, a);
+    if (plan.decode_ns == 2)
+        return plan.decode_ch == 2 ? launch_w4_decode<P, 2, 2>(plan, st, a) : launch_w4_decode<P, 2, 1>(plan, st, a);
+    return plan.decode_ch == 2 ? launch_w4_decode<P, 1, 2>(plan, st, a) : launch_w4_decode<P, 1, 1>(plan, st, a);
 }
 
 template <int R, int NS>

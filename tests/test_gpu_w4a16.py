@@ -102,17 +102,19 @@ def test_one_hot_decode_row(k):
 
 
 DECODE_CASES = [
-    # (M, K, N, env): token groups P = 4 / 8 / 16 with 1, 2, 4 or 8 super blocks per wave
+    # (M, K, N, env): token groups P = 4 / 8 / 16, whole and partial super blocks
     (1, 512, 384, None), (3, 2048, 1024, None), (4, 16384, 512, None), (2, 7168, 2048, None),
-    (5, 1024, 384, None), (8, 7168, 1024, None), (6, 4096, 2048, None), (7, 32768, 256, None),
-    (12, 1024, 1024, None), (16, 2048, 384, None), (16, 512, 2048, None), (9, 8192, 1024, None),
-    # K that does not split into equal slices: the streaming kernel
-    (1, 8576, 2048, None), (16, 8576, 1024, None),
+    (5, 1152, 384, None), (8, 7168, 1024, None), (6, 4096, 2048, None), (7, 32768, 256, None),
+    (12, 1024, 1024, None), (16, 2048, 384, None), (16, 640, 2048, None), (9, 8576, 1024, None),
+    (1, 8576, 2048, None), (1, 896, 384, None),
+    # the streaming kernel at decode sizes
     (1, 7168, 2048, {"FP8BS_W4_DECODE": "0"}), (5, 1152, 1024, {"FP8BS_W4_DECODE": "0"}),
-    # strips per workgroup with ragged tails
-    (1, 7168, 2048, {"FP8BS_W4_DECODE_SPW": "5"}), (8, 8192, 2048, {"FP8BS_W4_DECODE_SPW": "7"}),
-    (2, 2048, 1024, {"FP8BS_W4_DECODE_SPW": "1"}), (3, 1024, 1152, {"FP8BS_W4_DECODE_SPW": "3"}),
-    (16, 512, 1024, {"FP8BS_W4_DECODE_SPW": "9"}),
+    # strips per workgroup, super blocks per load batch, waves (uneven splits)
+    (1, 7168, 2048, {"FP8BS_W4_DECODE_NS": "1", "FP8BS_W4_DECODE_CH": "1"}),
+    (2, 2048, 1152, {"FP8BS_W4_DECODE_NS": "4"}), (7, 1280, 384, {"FP8BS_W4_DECODE_NS": "4"}),
+    (3, 1024, 1024, {"FP8BS_W4_DECODE_NS": "1", "FP8BS_W4_DECODE_CH": "2"}),
+    (16, 512, 1024, {"FP8BS_W4_DECODE_WAVES": "3"}), (1, 896, 384, {"FP8BS_W4_DECODE_WAVES": "2"}),
+    (4, 7168, 1024, {"FP8BS_W4_DECODE_WAVES": "5", "FP8BS_W4_DECODE_CH": "2"}),
 ]
 
 
