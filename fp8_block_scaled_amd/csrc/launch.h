@@ -69,6 +69,7 @@ struct W4Plan {
     int decode_ns;       //   strips per workgroup (1, 2 or 4)
     int decode_ch;       //   super blocks per load batch (1 or 2)
     int64_t decode_wgs;
+    int tile;            // > 0: LDS-tiled kernel, BM * 1000 + BN
 };
 
 W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus);

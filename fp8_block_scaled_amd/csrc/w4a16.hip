@@ -42,6 +42,7 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 typedef float v8f __attribute__((ext_vector_type(8)));
 
 constexpr int kW4MaxWaves = 8;
+constexpr int64_t kW4StreamMaxM = 64;      // above: LDS-tiled kernel
 
 struct W4Args {
     const uint8_t* w;        // [N, K/2] packed codes
@@ -304,6 +305,149 @@ __global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_decode_kernel(W4Args a
     }
 }
 
+// Prefill and batched decode (M > 64): LDS-tiled bf16 MFMA.
+//
+// A workgroup of 8 waves computes a BM x BN tile of y; its waves form a
+// (BM / WM) x (BN / WN) grid of WM x WN wave tiles.  K advances in steps of 64:
+// the next step's activations (BM x 64 BF16), codes (BN x 32 bytes) and group
+// scales (BN x 4 bytes) are loaded into registers while the current step is
+// computed from LDS, then written to the other half of a double buffer; one
+// barrier per step.
+//
+// k of (MFMA kk < 2, lane group g, element e) = 16 g + 8 kk + e within the step,
+// so a lane's codes for both MFMAs of a column are 8 contiguous bytes of one group
+// of 16 (one LDS read, one scale byte), dequantized in registers (exact, as above)
+// and used against all WM / 16 activation fragments of the wave.  Activations sit in
+// LDS as 16-byte chunks (8 k of one row), chunk c of row i at slot c * BM + (i ^ c):
+// an A fragment (16 rows, one chunk) is 256 contiguous bytes, and the 8 threads that
+// stage one row's 128 bytes write 8 different bank groups.  Rows past M are loaded
+// from row M - 1 and not stored; weight rows past N from row N - 1.
+constexpr int kW4TileK = 64;
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(512) void w4a16_tile_kernel(W4Args a, int64_t tiles_n) {
+    static_assert((BM / WM) * (BN / WN) == 8, "8 waves per workgroup");
+    constexpr int TM = WM / 16, TN = WN / 16;                 // MFMA tiles per wave
+    constexpr int A_PIECES = BM * 8 / 512;                     // 16-byte activation pieces per thread
+    constexpr int A_BYTES = BM * 128, B_BYTES = BN * 32, S_BYTES = BN * 4;
+    constexpr int BUF = A_BYTES + B_BYTES + S_BYTES;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // [2][BUF]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / (BN / WN), wn = wave % (BN / WN);
+    const int g = lane >> 4, r = lane & 15;
+    const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+    const int64_t KS = a.K / kW4TileK;
+
+    // Staging assignments.
+    const uint16_t* xsrc[A_PIECES];
+    int adst[A_PIECES];
+#pragma unroll
+    for (int i = 0; i < A_PIECES; ++i) {
+        const int p = tid + 512 * i;
+        const int row = p >> 3, c = p & 7;
+        const int64_t m = m0 + row < a.M ? m0 + row : a.M - 1;
+        xsrc[i] = a.x + m * a.K + 8 * c;
+        adst[i] = (c * BM + (row ^ c)) * 16;
+    }
+    const bool has_b = tid < BN * 2;
+    const bool has_s = tid < BN;
+    const uint8_t* wsrc;
+    const uint8_t* ssrc;
+    {
+        const int brow = tid >> 1, half = tid & 1;
+        const int64_t n = n0 + brow < a.N ? n0 + brow : a.N - 1;
+        wsrc = a.w + n * (a.K / 2) + 16 * half;
+        const int64_t ns = n0 + tid < a.N ? n0 + tid : a.N - 1;
+        ssrc = a.bs + (has_s ? ns : n0) * (a.K / 16);
+    }
+    v4i ra[A_PIECES], rb = {0, 0, 0, 0};
+    uint32_t rs = 0;
+    auto gload = [&](int64_t s) {
+        const int64_t k0 = s * kW4TileK;
+#pragma unroll
+        for (int i = 0; i < A_PIECES; ++i) ra[i] = *reinterpret_cast<const v4i*>(xsrc[i] + k0);
+        if (has_b) rb = *reinterpret_cast<const v4i*>(wsrc + k0 / 2);
+        if (has_s) rs = *reinterpret_cast<const uint32_t*>(ssrc + k0 / 16);
+    };
+    auto lstore = [&](int buf) {
+        uint8_t* base = smem + buf * BUF;
+#pragma unroll
+        for (int i = 0; i < A_PIECES; ++i) *reinterpret_cast<v4i*>(base + adst[i]) = ra[i];
+        if (has_b) *reinterpret_cast<v4i*>(base + A_BYTES + tid * 16) = rb;
+        if (has_s) *reinterpret_cast<uint32_t*>(base + A_BYTES + B_BYTES + tid * 4) = rs;
+    };
+
+    v4f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn) acc[i][jn] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int64_t s = 0; s < KS; ++s) {
+        const int buf = (int)(s & 1);
+        if (s + 1 < KS) gload(s + 1);
+        const uint8_t* base = smem + buf * BUF;
+        // Dequantized B operands of the wave's TN column tiles, both MFMAs of the step.
+        v8bf bq[TN][2];
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn) {
+            const int col = wn * WN + 16 * jn + r;
+            const uint2 c = *reinterpret_cast<const uint2*>(base + A_BYTES + col * 32 + 8 * g);
+            const uint32_t sw = *reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES + col * 4);
+            const float sc = __builtin_amdgcn_cvt_f32_fp8((int)(sw >> (8 * g)), 0);
+            bq[jn][0] = dequant8(c.x, sc);
+            bq[jn][1] = dequant8(c.y, sc);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int c = 2 * g + kk;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * WM + 16 * i + r;
+                const v4i av = *reinterpret_cast<const v4i*>(base + (c * BM + (row ^ c)) * 16);
+#pragma unroll
+                for (int jn = 0; jn < TN; ++jn)
+                    acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(av), bq[jn][kk], acc[i][jn], 0, 0, 0);
+            }
+        }
+        if (s + 1 < KS) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t m = m0 + wm * WM + 16 * i + 4 * g + e;
+                const int64_t n = n0 + wn * WN + 16 * jn + r;
+                if (m < a.M && n < a.N) a.y[m * a.N + n] = (uint16_t)f32_to_bf16_rne(a.g * acc[i][jn][e]);
+            }
+}
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_w4_tile(int64_t M, int64_t N, hipStream_t st, const W4Args& a) {
+    constexpr unsigned lds = 2 * (BM * 128 + BN * 32 + BN * 4);
+    static bool attr_set = false;            // idempotent; a race only repeats the call
+    if (lds > 65536 && !attr_set) {
+        const hipError_t e = hipFuncSetAttribute((const void*)w4a16_tile_kernel<BM, BN, WM, WN>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    hipLaunchKernelGGL((w4a16_tile_kernel<BM, BN, WM, WN>), dim3((unsigned)(tiles_m * tiles_n)), dim3(512), lds, st, a,
+                       tiles_n);
+    return hipGetLastError();
+}
+
 W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus) {
     W4Plan p{};
     p.groups = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
@@ -320,6 +464,21 @@ W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus) {
     if (const char* e = getenv("FP8BS_W4_WAVES")) {         // tuning hook
         const int v = atoi(e);
         if (v >= 1 && v <= kW4MaxWaves) p.waves = v;
+    }
+    // M > 64: LDS-tiled kernel, the largest tile that still gives (nearly) every CU
+    // a workgroup.
+    if (M > kW4StreamMaxM) {
+        const int64_t enough = cus - cus / 8;
+        auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+        if (tiles(256, 256) >= enough) p.tile = 256256;
+        else if (tiles(128, 256) >= enough) p.tile = 128256;
+        else if (tiles(128, 128) >= enough) p.tile = 128128;
+        else p.tile = 64128;
+        if (const char* e = getenv("FP8BS_W4_TILE")) {       // tuning hook
+            const int v = atoi(e);
+            if (v == 256256 || v == 128256 || v == 128128 || v == 64128) p.tile = v;
+        }
+        return p;
     }
     // Decode: K chunks folded into the MFMA; NS strips of P columns per workgroup.
     const char* de = getenv("FP8BS_W4_DECODE");              // tuning hook: 0 = stream kernel
@@ -399,6 +558,13 @@ hipError_t launch_w4a16(const W4Plan& plan, const void* x, const void* w, const 
     a.K = K;
     a.KB = plan.kblocks;
     a.strips = plan.strips;
+    switch (plan.tile) {
+        case 256256: return launch_w4_tile<256, 256, 128, 64>(M, N, st, a);
+        case 128256: return launch_w4_tile<128, 256, 64, 64>(M, N, st, a);
+        case 128128: return launch_w4_tile<128, 128, 64, 32>(M, N, st, a);
+        case 64128: return launch_w4_tile<64, 128, 32, 32>(M, N, st, a);
+        default: break;
+    }
     if (plan.decode_p > 0) {
         a.strips = N / plan.decode_p;        // strips of P columns
         switch (plan.decode_p) {

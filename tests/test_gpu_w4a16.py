@@ -128,6 +128,15 @@ def test_decode_schedules(M, K, N, env, monkeypatch):
     check(x, w4, bs, np.float32(2.0e-3), f"schedule {env}")
 
 
+@pytest.mark.parametrize("tile", ["256256", "128256", "128128", "64128"])
+@pytest.mark.parametrize("M,N,K", [(65, 384, 512), (300, 1024, 1152), (513, 384, 2048), (1000, 640, 256)])
+def test_tile_configs(tile, M, N, K, monkeypatch):
+    """Every LDS tile shape, with M and N tails that are not tile multiples."""
+    monkeypatch.setenv("FP8BS_W4_TILE", tile)
+    x, w4, bs = random_case(M, N, K, seed=M + N + K + int(tile))
+    check(x, w4, bs, np.float32(1.5e-3), f"tile {tile}")
+
+
 def test_global_scale_sign_and_zero():
     x, w4, bs = random_case(24, 384, 512, seed=5)
     y1 = gpu(x, w4, bs, np.float32(0.5))
