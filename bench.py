@@ -18,7 +18,10 @@ alone, K launches, and replayed between HIP events on the stream it runs on,
 giving its average duration for the roofline.
 
 Printed: ONE JSON line.  Besides the contract fields it carries the other
-workloads' numbers ("workloads"), measured the same way.
+workloads' numbers ("workloads"), measured the same way, and those of the NVFP4
+weight-only linear ("w4a16": one nvfp4_w4a16_linear launch per step, graph-timed,
+weights rotated over copies like the FP8 weights).  ``--workload w4a16_...`` times
+one NVFP4 workload alone.
 """
 
 import argparse
@@ -42,13 +45,22 @@ KERNEL_SOURCES = {
     "decode": ["gemm_decode.hip", "launch.h", "device_common.h", "api.hip"],
     "mid": ["gemm_mid.hip", "launch.h", "device_common.h", "api.hip"],
     "prefill": ["gemm_prefill.hip", "launch.h", "device_common.h", "api.hip"],
+    "w4a16": ["w4a16.hip", "launch.h", "device_common.h", "api.hip"],
 }
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
+W4_METRIC = "NVFP4 W4A16 linear: GB/s (decode, M<=64) and TFLOP/s (M>64), % of roofline"
 DECODE_MAX_M = 16               # block_linear takes the decode kernel for M <= 16,
 MID_MAX_M = 64                  # the mid-size kernel for M <= 64, else the prefill tiles
 
 
 def gemm_kind(M):
     return "decode" if M <= DECODE_MAX_M else ("mid" if M <= MID_MAX_M else "prefill")
+
+
+def kernel_kind(wl):
+    """Source set of the kernel that runs workload ``wl``."""
+    from synth import W4A16_WORKLOADS
+    return "w4a16" if wl.name in W4A16_WORKLOADS else gemm_kind(wl.M)
 
 
 def kernel_source_hash(kind):
@@ -251,6 +263,87 @@ def time_m_sweep(Ms=(32, 64, 128, 512, 2048), N=7168, K=7168, copies=8, steps=40
     return out
 
 
+class W4Case:
+    """Device-resident inputs of one NVFP4 W4A16 workload: packed codes and group scales
+    (rotated over copies so that the weights touched between two uses of one copy exceed
+    twice the Infinity Cache), BF16 activations, a preallocated output."""
+
+    def __init__(self, wl):
+        import numpy as np
+        import torch
+        import synth
+        self.wl = wl
+        w4, bs, g = synth.w4a16_weight(wl)
+        wbytes = w4.nbytes + bs.nbytes
+        self.copies = max(1, min(16, -(-2 * MALL_BYTES // wbytes)))
+        self.w4 = [torch.from_numpy(w4).cuda()]
+        self.bs = [torch.from_numpy(bs).cuda()]
+        for _ in range(self.copies - 1):
+            self.w4.append(self.w4[0].clone())
+            self.bs.append(self.bs[0].clone())
+        self.g = float(g)
+        self.x = dev_bf16(synth.w4a16_activation_rows(wl, np.arange(wl.M)))
+        self.y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+
+    def gemm(self, i):
+        import fp8_block_scaled_amd as fb
+        c = i % self.copies
+        fb.nvfp4_linear(self.x, self.w4[c], self.bs[c], self.g, out=self.y)
+
+
+def time_w4(case, steps, warmup):
+    """Average duration of nvfp4_w4a16_linear: K launches captured in a HIP graph and
+    replayed between events on the stream they run on."""
+    import torch
+    for i in range(warmup):
+        case.gemm(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            case.gemm(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    us = _replay_ms(graph) * 1e3 / steps
+    del graph
+    return us
+
+
+def w4_roofline(wl, us, traffic):
+    """Weight streaming (M <= 64) against HBM, larger M against the dense BF16 MFMA peak."""
+    if wl.M <= 64:
+        achieved = wl.gemm_bytes() / (us * 1e-6) / 1e9
+        r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = wl.gemm_flops() / (us * 1e-6) / 1e12
+        r = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    r["traffic"] = traffic
+    return r
+
+
+def time_w4_all(steps, traffic_file, names=None):
+    """Every NVFP4 W4A16 workload (or the named ones): duration, rates and roofline."""
+    import torch
+    from synth import W4A16_WORKLOADS
+    out = {}
+    for name in names or W4A16_WORKLOADS:
+        wl = W4A16_WORKLOADS[name]
+        print(f"[bench] {name}: setup", file=sys.stderr, flush=True)
+        case = W4Case(wl)
+        us = time_w4(case, max(5, min(steps, 50 if wl.M > 64 else steps)), 3)
+        out[name] = {"M": wl.M, "K": wl.K, "N": wl.N, "us": round(us, 2),
+                     "GB/s": round(wl.gemm_bytes() / (us * 1e-6) / 1e9, 1),
+                     "TFLOP/s": round(wl.gemm_flops() / (us * 1e-6) / 1e12, 1),
+                     "roofline": w4_roofline(wl, us, load_traffic(traffic_file, wl)),
+                     "weight_copies_rotated": case.copies}
+        del case
+        torch.cuda.empty_cache()
+    return out
+
+
 def roofline_for(wl, gemm_us, traffic):
     if wl.M <= 16:
         achieved = wl.gemm_bytes() / (gemm_us * 1e-6) / 1e9
@@ -273,7 +366,7 @@ def load_traffic(path, wl):
     except (OSError, ValueError):
         return None
     ent = t.get("workloads", {}).get(wl.name)
-    if not ent or ent.get("kernel_source_hash") != kernel_source_hash(gemm_kind(wl.M)):
+    if not ent or ent.get("kernel_source_hash") != kernel_source_hash(kernel_kind(wl)):
         return None
     return ent.get("bytes_per_dispatch")
 
@@ -309,23 +402,35 @@ def make_traffic(directory, out_path):
     _, copy_write = one(os.path.join(directory, "copy", "write"), "copyBuffer", "WRITE_SIZE")
     f_fac, w_fac = copy_bytes / (copy_fetch * 1024), copy_bytes / (copy_write * 1024)
     doc = {"method": ("rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, on bench.py --workload W "
-                      "--no-others, kernels matching gemm_; KiB per dispatch x 1024 x the factor that "
-                      "maps the same counter onto a 512 MiB device copy's bytes"),
+                      "--no-others, kernels matching gemm_ (w4a16_ for the NVFP4 workloads); KiB per "
+                      "dispatch x 1024 x the factor that maps the same counter onto a 512 MiB device "
+                      "copy's bytes"),
            "copy_factor": {"FETCH_SIZE": round(f_fac, 4), "WRITE_SIZE": round(w_fac, 4)},
            "workloads": {}}
-    for name, wl in WORKLOADS.items():
+    from synth import W4A16_WORKLOADS
+    for name, wl in list(WORKLOADS.items()) + list(W4A16_WORKLOADS.items()):
         d = os.path.join(directory, name)
         if not os.path.isdir(d):
             continue
-        kf, fetch = one(os.path.join(d, "fetch"), "gemm_", "FETCH_SIZE")
-        kw, write = one(os.path.join(d, "write"), "gemm_", "WRITE_SIZE")
+        filt = "w4a16_" if name in W4A16_WORKLOADS else "gemm_"
+        kf, fetch = one(os.path.join(d, "fetch"), filt, "FETCH_SIZE")
+        kw, write = one(os.path.join(d, "write"), filt, "WRITE_SIZE")
         assert kf == kw, (kf, kw)
         total = fetch * 1024 * f_fac + write * 1024 * w_fac
         doc["workloads"][name] = {
-            "kernel": kf[0], "grid": int(kf[1]), "kernel_source_hash": kernel_source_hash(gemm_kind(wl.M)),
+            "kernel": kf[0], "grid": int(kf[1]), "kernel_source_hash": kernel_source_hash(kernel_kind(wl)),
             "fetch_kib": round(fetch, 1), "write_kib": round(write, 1),
             "bytes_per_dispatch": int(round(total)), "algorithmic_bytes": wl.gemm_bytes(),
             "ratio_to_algorithmic": round(total / wl.gemm_bytes(), 3)}
+    # Workloads not measured in this run keep their earlier entries (each entry's bytes
+    # are already scaled by the copy factor of its own run).
+    try:
+        with open(out_path) as fh:
+            old = json.load(fh).get("workloads", {})
+    except (OSError, ValueError):
+        old = {}
+    for name, ent in old.items():
+        doc["workloads"].setdefault(name, ent)
     with open(out_path, "w") as fh:
         json.dump(doc, fh, indent=1)
         fh.write("\n")
@@ -422,6 +527,18 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    from synth import W4A16_WORKLOADS
+    if args.workload in W4A16_WORKLOADS:
+        # One NVFP4 workload alone (used for its kernel profiles).
+        w4 = time_w4_all(args.steps, args.traffic_file, [args.workload])[args.workload]
+        print(json.dumps({"metric": W4_METRIC, "value": w4["roofline"]["achieved"],
+                          "unit": w4["roofline"]["unit"], "n_gpus": 1, "steps": args.steps,
+                          "warmup": 3, "ms_per_step": round(w4["us"] * 1e-3, 5), "higher_is_better": True,
+                          "scaling": "weak", "vs_baseline": None, "dtype": "bf16 x nvfp4 (fp32 accumulate)",
+                          "data": "synthetic (seeded; Philox per-row streams)",
+                          "config": {"workload": args.workload, "M": w4["M"], "K": w4["K"], "N": w4["N"]},
+                          "roofline": w4["roofline"], "cpu_baseline": None}), flush=True)
+        return 0
     wl = WORKLOADS[args.workload]
     print(f"[bench] {wl.name}: setup", file=sys.stderr, flush=True)
     case = make_case(wl)
@@ -471,6 +588,7 @@ def main():
         out["workloads"] = others
         print("[bench] M sweep", file=sys.stderr, flush=True)
         out["m_sweep"] = time_m_sweep()
+        out["w4a16"] = time_w4_all(args.steps, args.traffic_file)
         print("[bench] rmsnorm_quant", file=sys.stderr, flush=True)
         out["rmsnorm_quant"] = {name: time_rmsnorm_quant(WORKLOADS[name], 50 if name == "prefill_oproj" else 200)
                                 for name in ("decode_qkv", "prefill_oproj")}

@@ -312,7 +312,8 @@ __global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_decode_kernel(W4Args a
 // the next step's activations (BM x 64 BF16), codes (BN x 32 bytes) and group
 // scales (BN x 4 bytes) are loaded into registers while the current step is
 // computed from LDS, then written to the other half of a double buffer; one
-// barrier per step.
+// barrier per step.  Smaller tiles compute less per step, so their loads are
+// requested DEPTH steps ahead (DEPTH register sets) to cover the memory latency.
 //
 // k of (MFMA kk < 2, lane group g, element e) = 16 g + 8 kk + e within the step,
 // so a lane's codes for both MFMAs of a column are 8 contiguous bytes of one group
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_decode_kernel(W4Args a
 // from row M - 1 and not stored; weight rows past N from row N - 1.
 constexpr int kW4TileK = 64;
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int DEPTH>
 __global__ __launch_bounds__(512) void w4a16_tile_kernel(W4Args a, int64_t tiles_n) {
     static_assert((BM / WM) * (BN / WN) == 8, "8 waves per workgroup");
     constexpr int TM = WM / 16, TN = WN / 16;                 // MFMA tiles per wave
@@ -363,21 +364,23 @@ __global__ __launch_bounds__(512) void w4a16_tile_kernel(W4Args a, int64_t tiles
         const int64_t ns = n0 + tid < a.N ? n0 + tid : a.N - 1;
         ssrc = a.bs + (has_s ? ns : n0) * (a.K / 16);
     }
-    v4i ra[A_PIECES], rb = {0, 0, 0, 0};
-    uint32_t rs = 0;
-    auto gload = [&](int64_t s) {
+    // DEPTH register sets: step s + DEPTH is requested while step s is computed.
+    v4i ra[DEPTH][A_PIECES], rb[DEPTH];
+    uint32_t rs[DEPTH];
+    auto gload = [&](int d, int64_t s) {
+        s = s < KS ? s : KS - 1;             // past the end: a repeated (cached) load, never stored
         const int64_t k0 = s * kW4TileK;
 #pragma unroll
-        for (int i = 0; i < A_PIECES; ++i) ra[i] = *reinterpret_cast<const v4i*>(xsrc[i] + k0);
-        if (has_b) rb = *reinterpret_cast<const v4i*>(wsrc + k0 / 2);
-        if (has_s) rs = *reinterpret_cast<const uint32_t*>(ssrc + k0 / 16);
+        for (int i = 0; i < A_PIECES; ++i) ra[d][i] = *reinterpret_cast<const v4i*>(xsrc[i] + k0);
+        rb[d] = has_b ? *reinterpret_cast<const v4i*>(wsrc + k0 / 2) : v4i{0, 0, 0, 0};
+        rs[d] = has_s ? *reinterpret_cast<const uint32_t*>(ssrc + k0 / 16) : 0u;
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int d, int buf) {
         uint8_t* base = smem + buf * BUF;
 #pragma unroll
-        for (int i = 0; i < A_PIECES; ++i) *reinterpret_cast<v4i*>(base + adst[i]) = ra[i];
-        if (has_b) *reinterpret_cast<v4i*>(base + A_BYTES + tid * 16) = rb;
-        if (has_s) *reinterpret_cast<uint32_t*>(base + A_BYTES + B_BYTES + tid * 4) = rs;
+        for (int i = 0; i < A_PIECES; ++i) *reinterpret_cast<v4i*>(base + adst[i]) = ra[d][i];
+        if (has_b) *reinterpret_cast<v4i*>(base + A_BYTES + tid * 16) = rb[d];
+        if (has_s) *reinterpret_cast<uint32_t*>(base + A_BYTES + B_BYTES + tid * 4) = rs[d];
     };
 
     v4f acc[TM][TN];
@@ -386,12 +389,7 @@ __global__ __launch_bounds__(512) void w4a16_tile_kernel(W4Args a, int64_t tiles
 #pragma unroll
         for (int jn = 0; jn < TN; ++jn) acc[i][jn] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int64_t s = 0; s < KS; ++s) {
-        const int buf = (int)(s & 1);
-        if (s + 1 < KS) gload(s + 1);
+    auto compute = [&](int buf) {
         const uint8_t* base = smem + buf * BUF;
         // Dequantized B operands of the wave's TN column tiles, both MFMAs of the step.
         v8bf bq[TN][2];
@@ -416,8 +414,23 @@ __global__ __launch_bounds__(512) void w4a16_tile_kernel(W4Args a, int64_t tiles
                     acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(av), bq[jn][kk], acc[i][jn], 0, 0, 0);
             }
         }
-        if (s + 1 < KS) lstore(buf ^ 1);
-        __syncthreads();
+    };
+
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) gload(d, d);
+    lstore(0, 0);
+    __syncthreads();
+    for (int64_t s0 = 0; s0 < KS; s0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int64_t s = s0 + d;
+            if (s < KS) {                                        // uniform
+                gload(d, s + DEPTH);                             // set d held step s, already in LDS
+                compute((int)(s & 1));
+                if (s + 1 < KS) lstore((d + 1) % DEPTH, (int)((s + 1) & 1));
+                __syncthreads();
+            }
+        }
     }
 
 #pragma unroll
@@ -432,18 +445,18 @@ __global__ __launch_bounds__(512) void w4a16_tile_kernel(W4Args a, int64_t tiles
             }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int DEPTH>
 static hipError_t launch_w4_tile(int64_t M, int64_t N, hipStream_t st, const W4Args& a) {
     constexpr unsigned lds = 2 * (BM * 128 + BN * 32 + BN * 4);
     static bool attr_set = false;            // idempotent; a race only repeats the call
     if (lds > 65536 && !attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)w4a16_tile_kernel<BM, BN, WM, WN>,
+        const hipError_t e = hipFuncSetAttribute((const void*)w4a16_tile_kernel<BM, BN, WM, WN, DEPTH>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((w4a16_tile_kernel<BM, BN, WM, WN>), dim3((unsigned)(tiles_m * tiles_n)), dim3(512), lds, st, a,
+    hipLaunchKernelGGL((w4a16_tile_kernel<BM, BN, WM, WN, DEPTH>), dim3((unsigned)(tiles_m * tiles_n)), dim3(512), lds, st, a,
                        tiles_n);
     return hipGetLastError();
 }
@@ -486,7 +499,9 @@ W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus) {
         const int P = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
         p.decode_p = P;
         const int64_t strips = N / P;
-        p.decode_ns = strips >= 8 * (int64_t)cus ? 4 : 2;
+        // Four strips per workgroup once there are 12 per CU (gate/up: 4096 strips on
+        // 256 CUs); fewer (q/k/v: 2304) run faster with two (measured).
+        p.decode_ns = strips >= 12 * (int64_t)cus ? 4 : 2;
         if (const char* e = getenv("FP8BS_W4_DECODE_NS")) {   // tuning hook
             const int v = atoi(e);
             if (v == 1 || v == 2 || v == 4) p.decode_ns = v;
@@ -559,10 +574,10 @@ hipError_t launch_w4a16(const W4Plan& plan, const void* x, const void* w, const 
     a.KB = plan.kblocks;
     a.strips = plan.strips;
     switch (plan.tile) {
-        case 256256: return launch_w4_tile<256, 256, 128, 64>(M, N, st, a);
-        case 128256: return launch_w4_tile<128, 256, 64, 64>(M, N, st, a);
-        case 128128: return launch_w4_tile<128, 128, 64, 32>(M, N, st, a);
-        case 64128: return launch_w4_tile<64, 128, 32, 32>(M, N, st, a);
+        case 256256: return launch_w4_tile<256, 256, 128, 64, 1>(M, N, st, a);
+        case 128256: return launch_w4_tile<128, 256, 64, 64, 2>(M, N, st, a);
+        case 128128: return launch_w4_tile<128, 128, 64, 32, 3>(M, N, st, a);
+        case 64128: return launch_w4_tile<64, 128, 32, 32, 4>(M, N, st, a);
         default: break;
     }
     if (plan.decode_p > 0) {
