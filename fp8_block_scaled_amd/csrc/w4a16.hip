@@ -326,10 +326,13 @@ __global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_decode_kernel(W4Args a
 constexpr int kW4TileK = 64;
 
 template <int BM, int BN, int WM, int WN, int DEPTH>
-__global__ __launch_bounds__(512) void w4a16_tile_kernel(W4Args a, int64_t tiles_n) {
-    static_assert((BM / WM) * (BN / WN) == 8, "8 waves per workgroup");
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w4a16_tile_kernel(W4Args a, int64_t tiles_n) {
+    constexpr int NT = (BM / WM) * (BN / WN) * 64;            // threads
+    static_assert(NT == 256 || NT == 512, "4 or 8 waves per workgroup");
+    static_assert((BN * 2) % NT == 0 || BN * 2 < NT, "code pieces per thread");
     constexpr int TM = WM / 16, TN = WN / 16;                 // MFMA tiles per wave
-    constexpr int A_PIECES = BM * 8 / 512;                     // 16-byte activation pieces per thread
+    constexpr int A_PIECES = BM * 8 / NT;                      // 16-byte activation pieces per thread
+    constexpr int B_PIECES = BN * 2 > NT ? BN * 2 / NT : 1;    // 16-byte code pieces per thread
     constexpr int A_BYTES = BM * 128, B_BYTES = BN * 32, S_BYTES = BN * 4;
     constexpr int BUF = A_BYTES + B_BYTES + S_BYTES;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // [2][BUF]
@@ -347,39 +350,47 @@ __global__ __launch_bounds__(512) void w4a16_tile_kernel(W4Args a, int64_t tiles
     int adst[A_PIECES];
 #pragma unroll
     for (int i = 0; i < A_PIECES; ++i) {
-        const int p = tid + 512 * i;
+        const int p = tid + NT * i;
         const int row = p >> 3, c = p & 7;
         const int64_t m = m0 + row < a.M ? m0 + row : a.M - 1;
         xsrc[i] = a.x + m * a.K + 8 * c;
         adst[i] = (c * BM + (row ^ c)) * 16;
     }
-    const bool has_b = tid < BN * 2;
+    const bool has_b = tid < BN * 2;          // with B_PIECES > 1 every thread has pieces
     const bool has_s = tid < BN;
-    const uint8_t* wsrc;
+    const uint8_t* wsrc[B_PIECES];
     const uint8_t* ssrc;
-    {
-        const int brow = tid >> 1, half = tid & 1;
+#pragma unroll
+    for (int i = 0; i < B_PIECES; ++i) {
+        const int p = tid + NT * i;
+        const int brow = p >> 1, half = p & 1;
         const int64_t n = n0 + brow < a.N ? n0 + brow : a.N - 1;
-        wsrc = a.w + n * (a.K / 2) + 16 * half;
+        wsrc[i] = a.w + n * (a.K / 2) + 16 * half;
+    }
+    {
         const int64_t ns = n0 + tid < a.N ? n0 + tid : a.N - 1;
         ssrc = a.bs + (has_s ? ns : n0) * (a.K / 16);
     }
     // DEPTH register sets: step s + DEPTH is requested while step s is computed.
-    v4i ra[DEPTH][A_PIECES], rb[DEPTH];
+    v4i ra[DEPTH][A_PIECES], rb[DEPTH][B_PIECES];
     uint32_t rs[DEPTH];
     auto gload = [&](int d, int64_t s) {
         s = s < KS ? s : KS - 1;             // past the end: a repeated (cached) load, never stored
         const int64_t k0 = s * kW4TileK;
 #pragma unroll
         for (int i = 0; i < A_PIECES; ++i) ra[d][i] = *reinterpret_cast<const v4i*>(xsrc[i] + k0);
-        rb[d] = has_b ? *reinterpret_cast<const v4i*>(wsrc + k0 / 2) : v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < B_PIECES; ++i)
+            rb[d][i] = has_b ? *reinterpret_cast<const v4i*>(wsrc[i] + k0 / 2) : v4i{0, 0, 0, 0};
         rs[d] = has_s ? *reinterpret_cast<const uint32_t*>(ssrc + k0 / 16) : 0u;
     };
     auto lstore = [&](int d, int buf) {
         uint8_t* base = smem + buf * BUF;
 #pragma unroll
         for (int i = 0; i < A_PIECES; ++i) *reinterpret_cast<v4i*>(base + adst[i]) = ra[d][i];
-        if (has_b) *reinterpret_cast<v4i*>(base + A_BYTES + tid * 16) = rb[d];
+#pragma unroll
+        for (int i = 0; i < B_PIECES; ++i)
+            if (has_b) *reinterpret_cast<v4i*>(base + A_BYTES + (tid + NT * i) * 16) = rb[d][i];
         if (has_s) *reinterpret_cast<uint32_t*>(base + A_BYTES + B_BYTES + tid * 4) = rs[d];
     };
 
@@ -391,19 +402,22 @@ __global__ __launch_bounds__(512) void w4a16_tile_kernel(W4Args a, int64_t tiles
 
     auto compute = [&](int buf) {
         const uint8_t* base = smem + buf * BUF;
-        // Dequantized B operands of the wave's TN column tiles, both MFMAs of the step.
-        v8bf bq[TN][2];
+        // Codes and group scale of the wave's TN column tiles: 8 bytes per lane and
+        // tile cover both MFMAs of the step; each half is dequantized just before use.
+        uint2 cw[TN];
+        float sc[TN];
 #pragma unroll
         for (int jn = 0; jn < TN; ++jn) {
             const int col = wn * WN + 16 * jn + r;
-            const uint2 c = *reinterpret_cast<const uint2*>(base + A_BYTES + col * 32 + 8 * g);
+            cw[jn] = *reinterpret_cast<const uint2*>(base + A_BYTES + col * 32 + 8 * g);
             const uint32_t sw = *reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES + col * 4);
-            const float sc = __builtin_amdgcn_cvt_f32_fp8((int)(sw >> (8 * g)), 0);
-            bq[jn][0] = dequant8(c.x, sc);
-            bq[jn][1] = dequant8(c.y, sc);
+            sc[jn] = __builtin_amdgcn_cvt_f32_fp8((int)(sw >> (8 * g)), 0);
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
+            v8bf bq[TN];
+#pragma unroll
+            for (int jn = 0; jn < TN; ++jn) bq[jn] = dequant8(kk ? cw[jn].y : cw[jn].x, sc[jn]);
             const int c = 2 * g + kk;
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
@@ -411,7 +425,7 @@ __global__ __launch_bounds__(512) void w4a16_tile_kernel(W4Args a, int64_t tiles
                 const v4i av = *reinterpret_cast<const v4i*>(base + (c * BM + (row ^ c)) * 16);
 #pragma unroll
                 for (int jn = 0; jn < TN; ++jn)
-                    acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(av), bq[jn][kk], acc[i][jn], 0, 0, 0);
+                    acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(av), bq[jn], acc[i][jn], 0, 0, 0);
             }
         }
     };
@@ -456,8 +470,8 @@ static hipError_t launch_w4_tile(int64_t M, int64_t N, hipStream_t st, const W4A
         attr_set = true;
     }
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((w4a16_tile_kernel<BM, BN, WM, WN, DEPTH>), dim3((unsigned)(tiles_m * tiles_n)), dim3(512), lds, st, a,
-                       tiles_n);
+    hipLaunchKernelGGL((w4a16_tile_kernel<BM, BN, WM, WN, DEPTH>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3((BM / WM) * (BN / WN) * 64), lds, st, a, tiles_n);
     return hipGetLastError();
 }
 
