@@ -123,3 +123,15 @@ def test_valid_call_without_a_gpu_reports_a_hip_error_not_a_crash(L):
 def test_workspace_size_query(L):
     for shape in ((8191, 7168, 7168), (4, 100, 128), (-1, 128, 128), (1, 9216, 7168), (8, 7168, 8192)):
         assert L.fp8_block_linear_workspace_size(*shape) == 0
+
+
+def test_nvfp4_binding_rejects_bad_tensors_before_any_gpu_call():
+    import torch
+    import fp8_block_scaled_amd as fb
+    x = torch.zeros((2, 256), dtype=torch.bfloat16)
+    w4 = torch.zeros((128, 128), dtype=torch.uint8)
+    bs = torch.zeros((128, 16), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU"):          # CPU tensors: no CPU path
+        fb.nvfp4_linear(x, w4, bs, 1.0)
+    with pytest.raises(TypeError):                        # not a tensor
+        fb.nvfp4_linear([[0.0] * 256] * 2, w4, bs, 1.0)

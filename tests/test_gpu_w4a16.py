@@ -153,6 +153,30 @@ def test_deterministic(M):
     assert_bits_equal(gpu(x, w4, bs, np.float32(1e-2)), gpu(x, w4, bs, np.float32(1e-2)), "repeat")
 
 
+@pytest.mark.parametrize("M", [1, 8, 40, 300])
+def test_graph_replay_matches_eager(M):
+    """nvfp4_linear captured in a HIP graph (as the bench runs it) reproduces the eager
+    output on every replay, with eager work in between: decode, streaming and tiled
+    schedules."""
+    x, w4, bs = random_case(M, 1024, 2048, seed=70 + M)
+    xd, wd, bd = dev_bf16(x), dev_u8(w4), dev_u8(bs)
+    y = torch.empty((M, 1024), dtype=torch.bfloat16, device="cuda")
+    banner(f"nvfp4_linear graph replay M={M}")
+    fb.nvfp4_linear(xd, wd, bd, 0.01, out=y)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fb.nvfp4_linear(xd, wd, bd, 0.01, out=y)
+    for i in range(4):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), i
+        fb.nvfp4_linear(xd, wd, bd, 0.5)       # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_empty_and_errors():
     e = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
     w4 = torch.zeros((128, 128), dtype=torch.uint8, device="cuda")
