@@ -1,4 +1,4 @@
-// NVFP4 weight-only linear (W4A16) on gfx950: weight-streaming kernel.
+// NVFP4 weight-only linear (W4A16) on gfx950.
 //
 // y[m, n] = g * sum_k x[m, k] * e2m1(code[n, k]) * e4m3(bs[n, k / 16])
 // ("Nanbeige4.3-33B-NVFP4-A16" model card, paragraph on the base revision and
@@ -14,16 +14,24 @@
 // needs no promotion step (the group scales are already inside the operand); the
 // global scale multiplies once at the end.
 //
-// Decode and batched decode (M up to 64) are bound by the weight stream: 0.5625
-// bytes per weight against 2 M flops.  One workgroup takes NS strips of 16 output
-// columns; its S waves split the 128-wide K blocks, each wave dequantizes a strip's
-// fragment once and multiplies it by R 16-token groups of the activations; partial
-// sums are added through LDS in a fixed order (deterministic).  A second grid
+// Three schedules, by M:
+//   M <= 16       w4a16_decode_kernel: K chunks folded into the MFMA, strips of
+//                 4 / 8 / 16 output columns, split-K inside the workgroup.
+//   16 < M <= 64  w4a16_stream_kernel (below): weights streamed once per workgroup,
+//                 each dequantized fragment multiplied by up to 4 token groups.
+//   M > 64        w4a16_tile_kernel: LDS-tiled, codes kept in LDS as FP4.
+// Every reduction runs in a fixed order: results are bitwise deterministic.
+//
+// Streaming kernel.  Decode and batched decode (M up to 64) are bound by the weight
+// stream: 0.5625 bytes per weight against 2 M flops.  One workgroup takes NS strips
+// of 16 output columns; its S waves split the 128-wide K blocks, each wave
+// dequantizes a strip's fragment once and multiplies it by R 16-token groups of the
+// activations; partial sums are added through LDS in a fixed order.  A second grid
 // dimension covers M in chunks of 16 R rows (rows past M are loaded from row M - 1
 // and not stored).
 //
-// MFMA operands per lane l (g = l / 16, r = l % 16) and K block kb: the lane loads
-// the 16 code bytes [64 kb + 16 g, +16) of weight row 16 st + r, i.e. codes
+// Its MFMA operands per lane l (g = l / 16, r = l % 16) and K block kb: the lane
+// loads the 16 code bytes [64 kb + 16 g, +16) of weight row 16 st + r, i.e. codes
 // k = 128 kb + 32 g + i, i < 32.  MFMA j (j < 4) takes codes i in [8 j, 8 j + 8)
 // (dword j; group 2 g + j / 2) as B column r, and activations
 // x[m][128 kb + 32 g + 8 j + e], e < 8, of token row m = 16 rho + r as A row r.
