@@ -27,6 +27,7 @@ __all__ = [
     "rmsnorm_quant",
     "block_linear",
     "nvfp4_linear",
+    "nvfp4_workspace_size",
     "workspace_size",
     "get_workspace",
     "Fp8bsError",
@@ -116,11 +117,11 @@ def workspace_size(M, N, K):
 
 
 def get_workspace(device, nbytes):
-    """A zero-filled workspace of at least ``nbytes`` for ``device``, cached per device.
+    """A workspace of at least ``nbytes`` for ``device``, cached per device.
 
-    The library leaves it zero-filled after every completed call, so it is reused
-    as is.  Calls on one device through this cache share it: they must be ordered
-    (one stream), as the library requires for a shared workspace.
+    No call reads workspace it has not written earlier in the same call, so the
+    buffer is reused as is.  Calls on one device through this cache share it: they
+    must be ordered (one stream), as the library requires for a shared workspace.
     """
     device = torch.device(device)
     key = device.index if device.index is not None else torch.cuda.current_device()
@@ -157,11 +158,18 @@ def block_linear(q, s, qw, ws, out=None, workspace=None):
     return y
 
 
-def nvfp4_linear(x, w4, bs, g, out=None):
+def nvfp4_workspace_size(M, N, K):
+    """Bytes of workspace nvfp4_linear's fastest schedule can use for this shape."""
+    return int(lib().nvfp4_w4a16_workspace_size(M, N, K))
+
+
+def nvfp4_linear(x, w4, bs, g, out=None, workspace=None):
     """y [M, N] bf16 = x @ W^T, W[n, k] = e2m1(w4 codes) * e4m3(bs[n, k/16]) * g.
 
     x: bf16 [M, K]; w4: uint8 [N, K/2] packed codes (element 2j in the low nibble of
     byte j); bs: uint8 (or float8_e4m3fn) [N, K/16] group scales; g: float global scale.
+    workspace: None (a cached per-device buffer of nvfp4_workspace_size bytes), or a
+    uint8 tensor (an empty one selects the schedules that need none).
     """
     _check_tensor(x, "x", _BF16, 2)
     _check_tensor(w4, "w4", (torch.uint8,), 2)
@@ -172,5 +180,11 @@ def nvfp4_linear(x, w4, bs, g, out=None):
         raise ValueError("w4 must be [N, K/2] and bs [N, K/16]")
     dev = x.device
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
-    _call("nvfp4_w4a16_linear", dev, x.data_ptr(), w4.data_ptr(), bs.data_ptr(), float(g), y.data_ptr(), M, N, K)
+    if workspace is None:
+        need = nvfp4_workspace_size(M, N, K) if K > 0 and K % 128 == 0 and N % 128 == 0 else 0
+        workspace = get_workspace(dev, need) if need else None
+    wptr = workspace.data_ptr() if workspace is not None and workspace.numel() else None
+    wbytes = workspace.numel() * workspace.element_size() if wptr is not None else 0
+    _call("nvfp4_w4a16_linear", dev, x.data_ptr(), w4.data_ptr(), bs.data_ptr(), float(g), y.data_ptr(), M, N, K,
+          wptr, wbytes)
     return y

@@ -33,7 +33,8 @@ SIGNATURES = {
     "fp8_rmsnorm_quant": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, _P, _I64, _I64, _P]),
     "fp8_block_linear": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "fp8_block_linear_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64]),
-    "nvfp4_w4a16_linear": (ctypes.c_int, [_P, _P, _P, ctypes.c_float, _P, _I64, _I64, _I64, _P]),
+    "nvfp4_w4a16_linear": (ctypes.c_int, [_P, _P, _P, ctypes.c_float, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    "nvfp4_w4a16_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "fp8bs_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fp8bs_abi_version": (ctypes.c_int, []),
 }

@@ -140,9 +140,10 @@ int fp8_block_linear(const void* q_e4m3, const float* s_f32, const void* w_e4m3,
 }
 
 int nvfp4_w4a16_linear(const void* x_bf16, const void* w_fp4, const void* bs_e4m3, float g, void* y_bf16,
-                       int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                       int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
     if (M < 0 || N < 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
-    if (!mul_ok(N, K) || !mul_ok(M, K) || !mul_ok(M * K, 2) || !mul_ok(M, N) || !mul_ok(M * N, 2))
+    if (!mul_ok(N, K) || !mul_ok(M, K) || !mul_ok(M * K, 2) || !mul_ok(M, N) || !mul_ok(M * N, 4))
         return FP8BS_ERR_SHAPE;
     if (M > INT32_MAX) return FP8BS_ERR_SHAPE;             // token rows are 32-bit in the kernels
     if (!std::isfinite(g)) return FP8BS_ERR_VALUE;
@@ -150,10 +151,13 @@ int nvfp4_w4a16_linear(const void* x_bf16, const void* w_fp4, const void* bs_e4m
     if (!x_bf16 || !w_fp4 || !bs_e4m3 || !y_bf16) return FP8BS_ERR_NULL;
     if (!aligned(x_bf16, 16) || !aligned(w_fp4, 16) || !aligned(bs_e4m3, 16) || !aligned(y_bf16, 16))
         return FP8BS_ERR_ALIGN;
+    if (workspace && !aligned(workspace, 256)) return FP8BS_ERR_WORKSPACE;
     int cus = 0;
     int rc = check_device(&cus);
     if (rc != FP8BS_OK) return rc;
-    const fp8bs::W4Plan plan = fp8bs::plan_w4a16(M, N, K, cus);
+    const fp8bs::W4Plan plan = fp8bs::plan_w4a16(M, N, K, cus, workspace ? workspace_bytes : 0);
+    if (plan.ksplit >= 2)                                  // one launch: M is at most a few hundred rows
+        return hip_status(fp8bs::launch_w4a16(plan, x_bf16, w_fp4, bs_e4m3, g, y_bf16, M, N, K, workspace, stream));
     // The grid covers at most kW4MaxChunks chunks of token rows per launch.
     const int64_t rows_per_launch = fp8bs::kW4MaxChunks * 16 * plan.groups;
     for (int64_t m0 = 0; m0 < M; m0 += rows_per_launch) {
@@ -161,10 +165,16 @@ int nvfp4_w4a16_linear(const void* x_bf16, const void* w_fp4, const void* bs_e4m
         fp8bs::W4Plan p = plan;
         p.m_chunks = (mm + 16 * p.groups - 1) / (16 * p.groups);
         const hipError_t e = fp8bs::launch_w4a16(p, (const uint16_t*)x_bf16 + m0 * K, w_fp4, bs_e4m3, g,
-                                                 (uint16_t*)y_bf16 + m0 * N, mm, N, K, stream);
+                                                 (uint16_t*)y_bf16 + m0 * N, mm, N, K, nullptr, stream);
         if (e != hipSuccess) return FP8BS_ERR_HIP;
     }
     return FP8BS_OK;
+}
+
+size_t nvfp4_w4a16_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return 0;
+    if (!mul_ok(M, N) || !mul_ok(M * N, 32)) return 0;
+    return fp8bs::w4a16_workspace_size(M, N, K);
 }
 
 }  // extern "C"

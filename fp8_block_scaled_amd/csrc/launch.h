@@ -70,11 +70,15 @@ struct W4Plan {
     int decode_ch;       //   super blocks per load batch (1 or 2)
     int64_t decode_wgs;
     int tile;            // > 0: LDS-tiled kernel, BM * 1000 + BN
+    int ksplit;          // >= 2: split-K over workgroups, FP32 partials in the workspace
 };
 
-W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus);
+// Workspace bytes the split-K schedule can use (0 when it never applies).
+size_t w4a16_workspace_size(int64_t M, int64_t N, int64_t K);
+
+W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus, size_t workspace_bytes);
 
 hipError_t launch_w4a16(const W4Plan& plan, const void* x, const void* w, const void* bs, float g, void* y,
-                        int64_t M, int64_t N, int64_t K, hipStream_t st);
+                        int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t st);
 
 }  // namespace fp8bs

@@ -51,6 +51,7 @@ typedef float v8f __attribute__((ext_vector_type(8)));
 
 constexpr int kW4MaxWaves = 8;
 constexpr int64_t kW4StreamMaxM = 64;      // above: LDS-tiled kernel
+constexpr int64_t kW4MaxSplit = 8;         // split-K ways at most
 
 struct W4Args {
     const uint8_t* w;        // [N, K/2] packed codes
@@ -334,7 +335,8 @@ __global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_decode_kernel(W4Args a
 constexpr int kW4TileK = 64;
 
 template <int BM, int BN, int WM, int WN, int DEPTH>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w4a16_tile_kernel(W4Args a, int64_t tiles_n) {
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w4a16_tile_kernel(W4Args a, int64_t tiles_n, int ksplit,
+                                                                               float* part) {
     constexpr int NT = (BM / WM) * (BN / WN) * 64;            // threads
     static_assert(NT == 256 || NT == 512, "4 or 8 waves per workgroup");
     static_assert((BN * 2) % NT == 0 || BN * 2 < NT, "code pieces per thread");
@@ -349,9 +351,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w4a16_tile_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / (BN / WN), wn = wave % (BN / WN);
     const int g = lane >> 4, r = lane & 15;
-    const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+    // Split-K: workgroup (tile, ks) covers K steps [KT ks / ksplit, KT (ks + 1) / ksplit)
+    // and, when part is given, stores FP32 partial sums there instead of y.
+    const int64_t tile = blockIdx.x / ksplit;
+    const int ks = (int)(blockIdx.x % ksplit);
+    const int64_t tm = tile / tiles_n, tn = tile % tiles_n;
     const int64_t m0 = tm * BM, n0 = tn * BN;
-    const int64_t KS = a.K / kW4TileK;
+    const int64_t KT = a.K / kW4TileK;
+    const int64_t s_begin = KT * ks / ksplit;
+    const int64_t KS = KT * (ks + 1) / ksplit - s_begin;          // steps of this workgroup (>= 1)
 
     // Staging assignments.
     const uint16_t* xsrc[A_PIECES];
@@ -384,7 +392,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w4a16_tile_kernel(
     uint32_t rs[DEPTH];
     auto gload = [&](int d, int64_t s) {
         s = s < KS ? s : KS - 1;             // past the end: a repeated (cached) load, never stored
-        const int64_t k0 = s * kW4TileK;
+        const int64_t k0 = (s_begin + s) * kW4TileK;
 #pragma unroll
         for (int i = 0; i < A_PIECES; ++i) ra[d][i] = *reinterpret_cast<const v4i*>(xsrc[i] + k0);
 #pragma unroll
@@ -489,12 +497,35 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w4a16_tile_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int64_t m = m0 + wm * WM + 16 * i + 4 * g + e;
                 const int64_t n = n0 + wn * WN + 16 * jn + r;
-                if (m < a.M && n < a.N) a.y[m * a.N + n] = (uint16_t)f32_to_bf16_rne(a.g * acc[i][jn][e]);
+                if (m < a.M && n < a.N) {
+                    if (part) part[((int64_t)ks * a.M + m) * a.N + n] = acc[i][jn][e];
+                    else a.y[m * a.N + n] = (uint16_t)f32_to_bf16_rne(a.g * acc[i][jn][e]);
+                }
             }
 }
 
+// Split-K: y = BF16(g * sum over ks of part[ks]) in the order ks = 0, 1, ...; four
+// neighbouring elements per thread (M N is a multiple of 128).
+__global__ __launch_bounds__(256) void w4a16_splitk_reduce_kernel(const float* part, int ksplit, int64_t mn, float g,
+                                                                 uint16_t* y) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= mn) return;
+    v4f sum = *reinterpret_cast<const v4f*>(part + i);
+    for (int ks = 1; ks < ksplit; ++ks) {
+        const v4f v = *reinterpret_cast<const v4f*>(part + (int64_t)ks * mn + i);
+        sum[0] += v[0];
+        sum[1] += v[1];
+        sum[2] += v[2];
+        sum[3] += v[3];
+    }
+    const uint32_t lo = f32_to_bf16_rne(g * sum[0]) | (f32_to_bf16_rne(g * sum[1]) << 16);
+    const uint32_t hi = f32_to_bf16_rne(g * sum[2]) | (f32_to_bf16_rne(g * sum[3]) << 16);
+    *reinterpret_cast<uint2*>(y + i) = make_uint2(lo, hi);
+}
+
 template <int BM, int BN, int WM, int WN, int DEPTH>
-static hipError_t launch_w4_tile(int64_t M, int64_t N, hipStream_t st, const W4Args& a) {
+static hipError_t launch_w4_tile(int64_t M, int64_t N, hipStream_t st, const W4Args& a, int ksplit = 1,
+                                 float* part = nullptr) {
     constexpr unsigned lds = 2 * (BM * 128 + BN * 32 + BN * 4);
     static bool attr_set = false;            // idempotent; a race only repeats the call
     if (lds > 65536 && !attr_set) {
@@ -504,12 +535,27 @@ static hipError_t launch_w4_tile(int64_t M, int64_t N, hipStream_t st, const W4A
         attr_set = true;
     }
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((w4a16_tile_kernel<BM, BN, WM, WN, DEPTH>), dim3((unsigned)(tiles_m * tiles_n)),
-                       dim3((BM / WM) * (BN / WN) * 64), lds, st, a, tiles_n);
+    hipLaunchKernelGGL((w4a16_tile_kernel<BM, BN, WM, WN, DEPTH>), dim3((unsigned)(tiles_m * tiles_n * ksplit)),
+                       dim3((BM / WM) * (BN / WN) * 64), lds, st, a, tiles_n, ksplit, part);
+    if (part) {
+        const int64_t mn = M * N;
+        hipLaunchKernelGGL(w4a16_splitk_reduce_kernel, dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, st,
+                           (const float*)part, ksplit, mn, a.g, a.y);
+    }
     return hipGetLastError();
 }
 
-W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus) {
+size_t w4a16_workspace_size(int64_t M, int64_t N, int64_t K) {
+    // Sized for the largest split any device up to 256 CUs would choose.
+    if (M <= kW4StreamMaxM || M <= 0 || N <= 0 || K <= 0) return 0;
+    const int64_t t2 = ((M + 127) / 128) * ((N + 255) / 256);
+    int64_t split = t2 < 256 ? 256 / t2 : 1;
+    if (split > kW4MaxSplit) split = kW4MaxSplit;
+    if (split > (K / kW4TileK) / 2) split = (K / kW4TileK) / 2;
+    return split >= 2 ? (size_t)split * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus, size_t workspace_bytes) {
     W4Plan p{};
     p.groups = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     p.strips = N / 16;
@@ -538,6 +584,23 @@ W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus) {
         if (const char* e = getenv("FP8BS_W4_TILE")) {       // tuning hook
             const int v = atoi(e);
             if (v == 256256 || v == 128256 || v == 128128 || v == 64128) p.tile = v;
+        }
+        // Too few 128 x 256 tiles for the CUs (a batch of up to a few hundred tokens):
+        // split K over workgroups when the caller gives room for the FP32 partial sums.
+        const int64_t t2 = ((M + 127) / 128) * ((N + 255) / 256);
+        const int64_t kt = K / kW4TileK;
+        int64_t split = t2 < enough ? cus / t2 : 1;
+        if (split > kW4MaxSplit) split = kW4MaxSplit;
+        if (split > kt / 2) split = kt / 2;                   // at least 2 K steps each
+        const int64_t room = (int64_t)(workspace_bytes / ((size_t)M * N * sizeof(float)));
+        if (split > room) split = room;
+        if (const char* e = getenv("FP8BS_W4_KSPLIT")) {     // tuning hook (within the room)
+            const int v = atoi(e);
+            if (v >= 1 && v <= kW4MaxSplit && v <= room && v <= kt) split = v;
+        }
+        if (split >= 2) {
+            p.tile = 128256;
+            p.ksplit = (int)split;
         }
         return p;
     }
@@ -608,7 +671,7 @@ static hipError_t launch_w4_r(const W4Plan& plan, dim3 grid, dim3 block, unsigne
 }
 
 hipError_t launch_w4a16(const W4Plan& plan, const void* x, const void* w, const void* bs, float gscale, void* y,
-                        int64_t M, int64_t N, int64_t K, hipStream_t st) {
+                        int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t st) {
     if (plan.strip_wgs == 0 || plan.m_chunks == 0) return hipSuccess;
     W4Args a;
     a.w = (const uint8_t*)w;
@@ -623,7 +686,9 @@ hipError_t launch_w4a16(const W4Plan& plan, const void* x, const void* w, const 
     a.strips = plan.strips;
     switch (plan.tile) {
         case 256256: return launch_w4_tile<256, 256, 128, 64, 1>(M, N, st, a);
-        case 128256: return launch_w4_tile<128, 256, 64, 64, 2>(M, N, st, a);
+        case 128256:
+            return plan.ksplit >= 2 ? launch_w4_tile<128, 256, 64, 64, 2>(M, N, st, a, plan.ksplit, (float*)workspace)
+                                    : launch_w4_tile<128, 256, 64, 64, 2>(M, N, st, a);
         case 128128: return launch_w4_tile<128, 128, 64, 32, 3>(M, N, st, a);
         case 64128: return launch_w4_tile<64, 128, 32, 32, 4>(M, N, st, a);
         default: break;

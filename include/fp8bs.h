@@ -145,14 +145,29 @@ size_t fp8_block_linear_workspace_size(int64_t M, int64_t N, int64_t K);
  *                       are outside the contract.
  *   g                   global scale, any finite float32 (else FP8BS_ERR_VALUE).
  *   y_bf16   [M, N]     output (out): fl32(g * acc) rounded to BF16 (nearest even).
+ *   workspace / workspace_bytes
+ *       Optional device scratch, sized by nvfp4_w4a16_workspace_size.  With it, a
+ *       batch too small to give every CU a tile (a few hundred tokens) splits K over
+ *       workgroups: FP32 partial sums go to the workspace and a second kernel adds
+ *       them in a fixed order.  NULL / 0, or a smaller workspace, selects a schedule
+ *       that fits (never an error); a workspace must be 256-byte aligned
+ *       (else FP8BS_ERR_WORKSPACE).  The caller owns it; calls that share one must
+ *       not overlap.
  * Shapes follow the shared rule (K and N multiples of 128).  Alignment: x, w, y and
  * bs 16-byte aligned.  Each product e2m1 * e4m3 is exact in BF16 and each product
  * with x exact in FP32; acc is their FP32 sum in an order fixed for a given
- * (M, N, K, device), so repeated calls give bitwise-identical outputs.  Accuracy:
- * |y - ref| <= 4e-3 |ref| + 1e-3 rms(ref) against the exact dequantize-and-matmul.
+ * (M, N, K, device, workspace size), so repeated calls give bitwise-identical
+ * outputs.  Accuracy: |y - ref| <= 4e-3 |ref| + 1e-3 rms(ref) against the exact
+ * dequantize-and-matmul.
  */
 int nvfp4_w4a16_linear(const void* x_bf16, const void* w_fp4, const void* bs_e4m3, float g,
-                       void* y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                       void* y_bf16, int64_t M, int64_t N, int64_t K,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace the fastest schedule of nvfp4_w4a16_linear can use for this shape
+ * on devices of up to 256 CUs (0 if none: decode shapes and large M; 0 for invalid
+ * shapes as well). */
+size_t nvfp4_w4a16_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /* Static, human-readable text for a status code. */
 const char* fp8bs_status_string(int status);

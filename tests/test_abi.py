@@ -96,21 +96,35 @@ def test_block_linear_validation(L):
 
 def test_nvfp4_linear_validation(L):
     f = L.nvfp4_w4a16_linear
-    assert f(A16, A16b, A16c, 1.0, A16d, 4, 100, 128, None) == ESHAPE
-    assert f(A16, A16b, A16c, 1.0, A16d, 4, 128, 112, None) == ESHAPE
-    assert f(A16, A16b, A16c, 1.0, A16d, 4, 128, 0, None) == ESHAPE
-    assert f(A16, A16b, A16c, 1.0, A16d, -1, 128, 128, None) == ESHAPE
-    assert f(A16, A16b, A16c, 1.0, A16d, 1 << 32, 128, 128, None) == ESHAPE     # 32-bit token rows
-    assert f(A16, A16b, A16c, float("nan"), A16d, 4, 128, 128, None) == EVAL
-    assert f(A16, A16b, A16c, float("inf"), A16d, 4, 128, 128, None) == EVAL
-    assert f(None, A16b, A16c, 1.0, A16d, 4, 128, 128, None) == ENULL
-    assert f(A16, A16b, None, 1.0, A16d, 4, 128, 128, None) == ENULL
-    assert f(A16 + 2, A16b, A16c, 1.0, A16d, 4, 128, 128, None) == EALIGN
-    assert f(A16, A16b + 8, A16c, 1.0, A16d, 4, 128, 128, None) == EALIGN
-    assert f(A16, A16b, A16c + 8, 1.0, A16d, 4, 128, 128, None) == EALIGN
-    assert f(A16, A16b, A16c, 1.0, A16d + 2, 4, 128, 128, None) == EALIGN
-    assert f(None, None, None, 1.0, None, 0, 128, 128, None) == OK          # M == 0
-    assert f(None, None, None, -2.5, None, 4, 0, 128, None) == OK           # N == 0
+    A = (A16, A16b, A16c)
+    assert f(*A, 1.0, A16d, 4, 100, 128, None, 0, None) == ESHAPE
+    assert f(*A, 1.0, A16d, 4, 128, 112, None, 0, None) == ESHAPE
+    assert f(*A, 1.0, A16d, 4, 128, 0, None, 0, None) == ESHAPE
+    assert f(*A, 1.0, A16d, -1, 128, 128, None, 0, None) == ESHAPE
+    assert f(*A, 1.0, A16d, 1 << 32, 128, 128, None, 0, None) == ESHAPE      # 32-bit token rows
+    assert f(*A, float("nan"), A16d, 4, 128, 128, None, 0, None) == EVAL
+    assert f(*A, float("inf"), A16d, 4, 128, 128, None, 0, None) == EVAL
+    assert f(None, A16b, A16c, 1.0, A16d, 4, 128, 128, None, 0, None) == ENULL
+    assert f(A16, A16b, None, 1.0, A16d, 4, 128, 128, None, 0, None) == ENULL
+    assert f(A16 + 2, A16b, A16c, 1.0, A16d, 4, 128, 128, None, 0, None) == EALIGN
+    assert f(A16, A16b + 8, A16c, 1.0, A16d, 4, 128, 128, None, 0, None) == EALIGN
+    assert f(A16, A16b, A16c + 8, 1.0, A16d, 4, 128, 128, None, 0, None) == EALIGN
+    assert f(A16, A16b, A16c, 1.0, A16d + 2, 4, 128, 128, None, 0, None) == EALIGN
+    assert f(*A, 1.0, A16d, 4, 128, 128, A16e + 16, 4096, None) == EWS
+    assert f(None, None, None, 1.0, None, 0, 128, 128, None, 0, None) == OK     # M == 0
+    assert f(None, None, None, -2.5, None, 4, 0, 128, None, 0, None) == OK      # N == 0
+
+
+def test_nvfp4_workspace_size_query(L):
+    q = L.nvfp4_w4a16_workspace_size
+    assert q(1, 9216, 7168) == 0 and q(16, 7168, 8192) == 0 and q(64, 7168, 7168) == 0    # decode / streaming
+    assert q(2048, 7168, 7168) == 0                                      # enough tiles without a split
+    assert q(128, 16384, 7168) == 4 * 128 * 16384 * 4                     # 64 tiles: split 4
+    assert q(100, 1024, 1152) == 8 * 100 * 1024 * 4                       # split capped at 8 ...
+    assert q(100, 1024, 256) == 2 * 100 * 1024 * 4                        # ... and at half the K steps
+    assert q(100, 1024, 128) == 0
+    for bad in ((-1, 128, 128), (4, 100, 128), (4, 128, 0)):
+        assert q(*bad) == 0
 
 
 def test_valid_call_without_a_gpu_reports_a_hip_error_not_a_crash(L):

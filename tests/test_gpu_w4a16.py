@@ -35,15 +35,19 @@ def random_case(M, N, K, seed, scale_codes=None):
     return x, w4, bs
 
 
-def gpu(x, w4, bs, g):
-    y = fb.nvfp4_linear(dev_bf16(x), dev_u8(w4), dev_u8(bs), g)
+def gpu(x, w4, bs, g, workspace=None):
+    y = fb.nvfp4_linear(dev_bf16(x), dev_u8(w4), dev_u8(bs), g, workspace=workspace)
     torch.cuda.synchronize()
     return host_u16(y)
 
 
-def check(x, w4, bs, g, what):
+def no_workspace():
+    return torch.empty(0, dtype=torch.uint8, device="cuda")
+
+
+def check(x, w4, bs, g, what, workspace=None):
     banner(f"nvfp4_linear {what} M={x.shape[0]} N={w4.shape[0]} K={x.shape[1]}")
-    y = gpu(x, w4, bs, g)
+    y = gpu(x, w4, bs, g, workspace)
     res = oracle.check_tolerance(y, oracle.linear_w4a16_ref(x, w4, bs, g))
     assert res["ok"], f"{what}: {res}"
     return y
@@ -134,7 +138,36 @@ def test_tile_configs(tile, M, N, K, monkeypatch):
     """Every LDS tile shape, with M and N tails that are not tile multiples."""
     monkeypatch.setenv("FP8BS_W4_TILE", tile)
     x, w4, bs = random_case(M, N, K, seed=M + N + K + int(tile))
-    check(x, w4, bs, np.float32(1.5e-3), f"tile {tile}")
+    check(x, w4, bs, np.float32(1.5e-3), f"tile {tile}", workspace=no_workspace())
+
+
+@pytest.mark.parametrize("M,N,K,split", [(65, 1024, 1152, None), (128, 2048, 2048, None), (200, 1024, 7168, None),
+                                         (300, 1152, 1024, None), (128, 1024, 7168, "2"), (100, 512, 3072, "3"),
+                                         (129, 768, 4096, "8"), (80, 256, 256, "4")])
+def test_split_k(M, N, K, split, monkeypatch):
+    """Split-K over workgroups (FP32 partials in the workspace, fixed-order sum)."""
+    if split:
+        monkeypatch.setenv("FP8BS_W4_KSPLIT", split)
+    assert fb.nvfp4_workspace_size(M, N, K) > 0 or split
+    x, w4, bs = random_case(M, N, K, seed=3 * M + N + K)
+    ws = torch.empty(8 * M * N * 4, dtype=torch.uint8, device="cuda")
+    y = check(x, w4, bs, np.float32(2.5e-3), f"split-K {split}", workspace=ws)
+    assert_bits_equal(gpu(x, w4, bs, np.float32(2.5e-3), ws), y, "split-K repeat")
+
+
+def test_split_k_workspace_sizes():
+    """A smaller workspace selects a smaller split (or none); every result is in
+    tolerance and the size query's workspace is enough for the default split."""
+    M, N, K = 128, 2048, 4096
+    x, w4, bs = random_case(M, N, K, seed=11)
+    ref = oracle.linear_w4a16_ref(x, w4, bs, np.float32(1e-2))
+    need = fb.nvfp4_workspace_size(M, N, K)
+    assert need > 0
+    for nbytes in (need, need // 2, 2 * M * N * 4, M * N * 4, 0):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        banner(f"nvfp4_linear split-K workspace {nbytes}")
+        res = oracle.check_tolerance(gpu(x, w4, bs, np.float32(1e-2), ws), ref)
+        assert res["ok"], (nbytes, res)
 
 
 def test_global_scale_sign_and_zero():
