@@ -386,8 +386,9 @@ def _counter_means(directory, name_filter):
 
 
 def make_traffic(directory, out_path):
-    """HBM bytes per GEMM dispatch = FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
-    scaled by what that counter reads for a plain device copy of known size."""
+    """HBM bytes per GEMM call = FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over
+    the kernels of one call), each scaled by what that counter reads for a plain device
+    copy of known size."""
     from synth import WORKLOADS
 
     def one(d, what, counter):
@@ -413,15 +414,23 @@ def make_traffic(directory, out_path):
         if not os.path.isdir(d):
             continue
         filt = "w4a16_" if name in W4A16_WORKLOADS else "gemm_"
-        kf, fetch = one(os.path.join(d, "fetch"), filt, "FETCH_SIZE")
-        kw, write = one(os.path.join(d, "write"), filt, "WRITE_SIZE")
-        assert kf == kw, (kf, kw)
+        # One call may launch several kernels (the NVFP4 split-K tile and its reduce):
+        # the call's bytes are the sum over them, the dominant one names the entry.
+        fm = _counter_means(os.path.join(d, "fetch"), filt)
+        wm = _counter_means(os.path.join(d, "write"), filt)
+        if not fm or set(fm) != set(wm):
+            raise SystemExit(f"{d}: fetch/write kernels differ: {sorted(fm)} vs {sorted(wm)}")
+        fetch = sum(v["FETCH_SIZE"] for v in fm.values())
+        write = sum(v["WRITE_SIZE"] for v in wm.values())
+        kf = max(fm, key=lambda k: fm[k]["FETCH_SIZE"])
         total = fetch * 1024 * f_fac + write * 1024 * w_fac
         doc["workloads"][name] = {
             "kernel": kf[0], "grid": int(kf[1]), "kernel_source_hash": kernel_source_hash(kernel_kind(wl)),
             "fetch_kib": round(fetch, 1), "write_kib": round(write, 1),
             "bytes_per_dispatch": int(round(total)), "algorithmic_bytes": wl.gemm_bytes(),
             "ratio_to_algorithmic": round(total / wl.gemm_bytes(), 3)}
+        if len(fm) > 1:
+            doc["workloads"][name]["kernels_per_call"] = sorted(k[0] for k in fm)
     # Workloads not measured in this run keep their earlier entries (each entry's bytes
     # are already scaled by the copy factor of its own run).
     try:
