@@ -108,8 +108,8 @@ int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, float eps, voi
 size_t fp8_block_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K <= 0 || N % 128 || K % 128 || !mul_ok(N, K) || !mul_ok(M, K) || !mul_ok(M, N))
         return 0;
-    // No current schedule needs scratch memory; the argument is kept in the ABI.
-    return 0;
+    if (!mul_ok(M * N, 32)) return 0;
+    return fp8bs::prefill_workspace_size(M, N, K);     // split-K partial sums (0 when unused)
 }
 
 int fp8_block_linear(const void* q_e4m3, const float* s_f32, const void* w_e4m3, const float* ws_f32,
@@ -126,17 +126,19 @@ int fp8_block_linear(const void* q_e4m3, const float* s_f32, const void* w_e4m3,
     int cus = 0;
     int rc = check_device(&cus);
     if (rc != FP8BS_OK) return rc;
-    (void)workspace_bytes;
     if (M <= fp8bs::kDecodeMaxM) {
         const fp8bs::DecodePlan plan = fp8bs::plan_decode(M, N, K, cus);
         return hip_status(
             fp8bs::launch_gemm_decode(plan, q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, stream));
     }
-    if (M <= fp8bs::kMidMaxM) {
+    // 24 < M <= 64 with a workspace: split-K tiles beat weight streaming.
+    if (M <= fp8bs::kMidMaxM &&
+        !(M > fp8bs::kSplitMinM && workspace && fp8bs::prefill_plan_split(M, N, K, cus, workspace_bytes) >= 2)) {
         const fp8bs::MidPlan plan = fp8bs::plan_mid(M, N, K, cus);
         return hip_status(fp8bs::launch_gemm_mid(plan, q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, stream));
     }
-    return hip_status(fp8bs::launch_gemm_prefill(q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, cus, stream));
+    return hip_status(fp8bs::launch_gemm_prefill(q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, cus, workspace,
+                                                 workspace ? workspace_bytes : 0, stream));
 }
 
 int nvfp4_w4a16_linear(const void* x_bf16, const void* w_fp4, const void* bs_e4m3, float g, void* y_bf16,

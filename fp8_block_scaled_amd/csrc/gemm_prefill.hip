@@ -43,6 +43,7 @@ namespace fp8bs {
 
 constexpr int kGroupRows = 8;
 constexpr int kXcds = 8;
+constexpr int kPrefillMaxSplit = 8;
 
 struct PrefillArgs {
     const uint8_t* w;
@@ -52,6 +53,8 @@ struct PrefillArgs {
     uint16_t* y;
     int64_t M, N, K, KB;
     int64_t tiles_m, tiles_n;
+    int ksplit;          // >= 1: K blocks split over this many workgroups per tile
+    float* part;         // split-K: FP32 partial sums [ksplit][M][N] (else nullptr)
 };
 
 // Bytes of one LDS stage: w tile, q tile, BM token scales, weight scales (one
@@ -88,7 +91,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
 
     // ---- tile selection: XCD-contiguous, grouped raster
     const int64_t T = a.tiles_m * a.tiles_n;
-    const int64_t b = blockIdx.x;
+    // Split-K: workgroup b covers K blocks [KB ks / ksplit, KB (ks + 1) / ksplit) of
+    // tile b / ksplit.
+    const int64_t b = blockIdx.x / a.ksplit;
+    const int ks = (int)(blockIdx.x % a.ksplit);
+    const int64_t kb0 = a.KB * ks / a.ksplit, kb1 = a.KB * (ks + 1) / a.ksplit;
     const int64_t xcd = b % kXcds, jx = b / kXcds;
     const int64_t per = T / kXcds, extra = T % kXcds;
     const int64_t t = xcd * per + (xcd < extra ? xcd : extra) + jx;
@@ -222,13 +229,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
 #pragma unroll
         for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    copy_stage(0, 0);
-    copy_scales(0, 0);
-    copy_wscales(0, 0);
-    warm(a.KB > 1 ? 1 : 0);
+    copy_stage(kb0, 0);
+    copy_scales(kb0, 0);
+    copy_wscales(kb0, 0);
+    warm(kb0 + 1 < kb1 ? kb0 + 1 : kb1 - 1);
 
-    for (int64_t kb = 0; kb < a.KB; ++kb) {
-        const int stage = (int)(kb & 1);
+    for (int64_t kb = kb0; kb < kb1; ++kb) {
+        const int stage = (int)((kb - kb0) & 1);
         // This wave's copies into `stage` (and the scale loads) have landed -- all
         // but the last load issued, the warm-up touch; the barrier makes everyone's
         // copies visible and frees the other stage.
@@ -240,7 +247,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
         asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        const bool more = kb + 1 < a.KB;
+        const bool more = kb + 1 < kb1;
         const uint8_t* wt = lds + stage * kStage;
         const uint8_t* xt = wt + BN * 128;
         v8i bf[TJ];
@@ -268,7 +275,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
             if (i == kCopyRows - 1) {
                 copy_scales(kn, stage ^ 1);
                 copy_wscales(kn, stage ^ 1);
-                warm(kb + 2 < a.KB ? kb + 2 : a.KB - 1);       // always one warm-up load last
+                warm(kb + 2 < kb1 ? kb + 2 : kb1 - 1);         // always one warm-up load last
             }
             const v8i af = af_next;
             if (i + 1 < TI) af_next = lds_frag(wt, wn * WTN + 16 * (i + 1) + r, g);
@@ -301,6 +308,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
             const int64_t n = n0 + wn * WTN + 16 * i + 4 * g;
+            if (a.part) {                                      // split-K partial sums
+                *reinterpret_cast<v4f*>(a.part + ((int64_t)ks * a.M + m) * a.N + n) = acc[i][j];
+                continue;
+            }
             uint2 o;
             o.x = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
             o.y = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
@@ -323,8 +334,9 @@ static hipError_t launch_tiles(PrefillArgs a, hipStream_t st) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((gemm_prefill_kernel<BM, BN, WM, WN, CLAMP>), dim3((unsigned)T), dim3(64 * WM * WN), lds,
-                       st, a);
+    hipLaunchKernelGGL((gemm_prefill_kernel<BM, BN, WM, WN, CLAMP>), dim3((unsigned)(T * a.ksplit)),
+                       dim3(64 * WM * WN), lds, st, a);
+    if (a.part) return launch_splitk_reduce(a.part, a.ksplit, a.M * a.N, 1.0f, a.y, st);
     return hipGetLastError();
 }
 
@@ -335,8 +347,39 @@ static hipError_t launch_shape(PrefillArgs a, hipStream_t st) {
     return launch_tiles<BM, BN, WM, WN, false>(a, st);
 }
 
+// Split-K ways for a shape whose 128 x 128 tiles leave CUs idle (0: none); the
+// workspace size query assumes up to 256 CUs.  Above kSplitMinM rows split-K tiles
+// beat the weight-streaming mid-size kernel (measured on the 7168 x 7168
+// projection: 25.0 against 28.7 us at M = 32, 26.7 against 49.6 us at M = 64).
+int prefill_split(int64_t M, int64_t N, int64_t K, int cus) {
+    if (M <= kSplitMinM) return 0;
+    const int64_t t = (M + 127) / 128 * (N / 128);
+    if (t >= cus - cus / 8) return 0;
+    int64_t split = cus / t;
+    if (split > kPrefillMaxSplit) split = kPrefillMaxSplit;
+    if (split > (K / kGroup) / 4) split = (K / kGroup) / 4;   // at least 4 K blocks each
+    return split >= 2 ? (int)split : 0;
+}
+
+int prefill_plan_split(int64_t M, int64_t N, int64_t K, int cus, size_t workspace_bytes) {
+    int split = prefill_split(M, N, K, cus);
+    const int64_t room = (int64_t)(workspace_bytes / ((size_t)M * N * sizeof(float)));
+    if (split > room) split = (int)room;
+    if (const char* e = getenv("FP8BS_PREFILL_KSPLIT")) {     // tuning hook (within the room)
+        const int v = atoi(e);
+        if (v >= 1 && v <= kPrefillMaxSplit && v <= room && v <= K / kGroup && M > kSplitMinM) split = v;
+    }
+    return split >= 2 ? split : 0;
+}
+
+size_t prefill_workspace_size(int64_t M, int64_t N, int64_t K) {
+    const int split = prefill_split(M, N, K, 256);
+    return split ? (size_t)split * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
 hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, const float* ws, void* y,
-                               int64_t M, int64_t N, int64_t K, int cus, hipStream_t st) {
+                               int64_t M, int64_t N, int64_t K, int cus, void* workspace, size_t workspace_bytes,
+                               hipStream_t st) {
     PrefillArgs a;
     a.w = (const uint8_t*)w;
     a.ws = ws;
@@ -347,6 +390,8 @@ hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, con
     a.N = N;
     a.K = K;
     a.KB = K / kGroup;
+    a.ksplit = 1;
+    a.part = nullptr;
     // Tile shape, 8 waves each: the largest of 256 x 256 (waves of 64 x 128),
     // 128 x 256 and 128 x 128 that still gives nearly every CU a tile (measured on
     // M = 129 .. 8191, N = K = 7168: a tile row of 256 wins only when there are
@@ -362,6 +407,15 @@ hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, con
     if (const char* e = getenv("FP8BS_PREFILL_TILE")) {
         const int t = atoi(e);
         if (t == 256128 || t == 128128 || (n256 && (t == 256256 || t == 128256))) tile = t;
+    }
+    // Few tiles (a batch of up to a few hundred tokens): with a workspace, split K
+    // over the workgroups of each 128 x 128 tile; FP32 partial sums, then a reduce
+    // kernel adds them in a fixed order.
+    const int split = prefill_plan_split(M, N, K, cus, workspace ? workspace_bytes : 0);
+    if (split >= 2) {
+        tile = 128128;
+        a.ksplit = split;
+        a.part = (float*)workspace;
     }
     switch (tile) {
         case 256256: return launch_shape<256, 256, 4, 2>(a, st);

@@ -34,6 +34,8 @@ hipError_t launch_gemm_decode(const DecodePlan& plan, const void* q, const float
 // ---- mid-size GEMM (kDecodeMaxM < M <= kMidMaxM): weight streaming, R token groups
 // (above 64 rows the 128 x 128 prefill tiles are faster)
 constexpr int kMidMaxM = 64;
+// Above this many rows a split-K prefill schedule (given a workspace) is used instead.
+constexpr int kSplitMinM = 24;
 
 struct MidPlan {
     int groups;          // R: 16-token groups per weight fragment (2, 4 or 8)
@@ -49,9 +51,18 @@ MidPlan plan_mid(int64_t M, int64_t N, int64_t K, int cus);
 hipError_t launch_gemm_mid(const MidPlan& plan, const void* q, const float* s, const void* w, const float* ws,
                            void* y, int64_t M, int64_t N, int64_t K, hipStream_t st);
 
-// ---- prefill GEMM (M > kMidMaxM): LDS-tiled FP8 MFMA
+// ---- prefill GEMM (M > kMidMaxM): LDS-tiled FP8 MFMA; with a workspace, split-K
+// for shapes whose tiles leave CUs idle
 hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, const float* ws, void* y,
-                               int64_t M, int64_t N, int64_t K, int cus, hipStream_t st);
+                               int64_t M, int64_t N, int64_t K, int cus, void* workspace, size_t workspace_bytes,
+                               hipStream_t st);
+size_t prefill_workspace_size(int64_t M, int64_t N, int64_t K);
+// Split-K ways launch_gemm_prefill uses for this shape and workspace (0: none).
+int prefill_plan_split(int64_t M, int64_t N, int64_t K, int cus, size_t workspace_bytes);
+
+// ---- split-K reduce: y = BF16(g * sum over ks < ksplit of part[ks]), in order
+// (part: FP32 [ksplit][mn], mn a multiple of 4; y: BF16 [mn])
+hipError_t launch_splitk_reduce(const float* part, int ksplit, int64_t mn, float g, uint16_t* y, hipStream_t st);
 
 // ---- NVFP4 weight-only linear (W4A16): weight streaming, R 16-token groups per
 // dequantized fragment, M covered in chunks of 16 R rows (second grid dimension)

@@ -107,11 +107,13 @@ int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, float eps,
  *   w_e4m3  [N, K]            weight codes;     ws_f32 [N/128, K/128] block scales.
  *   y_bf16  [M, N]            output (out), rounded to BF16 (nearest even) once.
  *   workspace / workspace_bytes
- *       Optional device scratch for schedules that need it, sized by
- *       fp8_block_linear_workspace_size.  The current schedules need none (the
- *       decode schedule reduces its split-K partial sums inside each workgroup), so
- *       the size query returns 0 and NULL / 0 may be passed.  When given it must be
- *       256-byte aligned; a workspace that is too small never causes an error.
+ *       Optional device scratch, sized by fp8_block_linear_workspace_size.  With it,
+ *       a batch too small to give every CU a tile (64 < M up to a few hundred tokens)
+ *       splits K over the workgroups of each tile: FP32 partial sums go to the
+ *       workspace and a second kernel adds them in a fixed order.  NULL / 0, or a
+ *       smaller workspace, selects a schedule that fits (never an error); it must be
+ *       256-byte aligned (else FP8BS_ERR_WORKSPACE).  Calls that share one must not
+ *       overlap.
  * Per 128-wide K block the FP32 partial product is multiplied by s[m, kb] *
  * ws[n/128, kb] and added to an FP32 accumulator.  The summation order is fixed
  * for a given (M, N, K, device, workspace size), so repeated calls give
@@ -123,9 +125,9 @@ int fp8_block_linear(const void* q_e4m3, const float* s_f32,
                      void* y_bf16, int64_t M, int64_t N, int64_t K,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace the fastest schedule of fp8_block_linear needs for this shape
- * (0 if none, which is the case for every shape in this version; 0 for invalid
- * shapes as well). */
+/* Bytes of workspace the fastest schedule of fp8_block_linear can use for this shape
+ * on devices of up to 256 CUs (0 if none: decode and mid-size shapes, and prefill
+ * shapes with enough tiles; 0 for invalid shapes as well). */
 size_t fp8_block_linear_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*

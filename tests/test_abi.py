@@ -117,7 +117,8 @@ def test_nvfp4_linear_validation(L):
 
 def test_nvfp4_workspace_size_query(L):
     q = L.nvfp4_w4a16_workspace_size
-    assert q(1, 9216, 7168) == 0 and q(16, 7168, 8192) == 0 and q(64, 7168, 7168) == 0    # decode / streaming
+    assert q(1, 9216, 7168) == 0 and q(16, 7168, 8192) == 0 and q(24, 7168, 7168) == 0    # decode / streaming
+    assert q(64, 7168, 7168) == 8 * 64 * 7168 * 4                        # split-K tiles above 24 rows
     assert q(2048, 7168, 7168) == 0                                      # enough tiles without a split
     assert q(128, 16384, 7168) == 4 * 128 * 16384 * 4                     # 64 tiles: split 4
     assert q(100, 1024, 1152) == 8 * 100 * 1024 * 4                       # split capped at 8 ...
@@ -135,8 +136,16 @@ def test_valid_call_without_a_gpu_reports_a_hip_error_not_a_crash(L):
 
 
 def test_workspace_size_query(L):
-    for shape in ((8191, 7168, 7168), (4, 100, 128), (-1, 128, 128), (1, 9216, 7168), (8, 7168, 8192)):
+    for shape in ((8191, 7168, 7168), (4, 100, 128), (-1, 128, 128), (1, 9216, 7168), (8, 7168, 8192),
+                  (24, 7168, 7168), (2048, 7168, 7168)):
         assert L.fp8_block_linear_workspace_size(*shape) == 0
+    assert L.fp8_block_linear_workspace_size(25, 7168, 7168) == 4 * 25 * 7168 * 4   # split-K above 24 rows
+    # 56 tiles of 128 x 128: split 4 (256 / 56), FP32 [4][M][N]
+    assert L.fp8_block_linear_workspace_size(128, 7168, 7168) == 4 * 128 * 7168 * 4
+    # capped at 8 ways and at a quarter of the K blocks
+    assert L.fp8_block_linear_workspace_size(100, 1024, 8192) == 8 * 100 * 1024 * 4
+    assert L.fp8_block_linear_workspace_size(100, 1024, 1024) == 2 * 100 * 1024 * 4
+    assert L.fp8_block_linear_workspace_size(100, 1024, 512) == 0
 
 
 def test_nvfp4_binding_rejects_bad_tensors_before_any_gpu_call():

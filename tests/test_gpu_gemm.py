@@ -164,12 +164,14 @@ def test_prefill_tile_shapes(tile, M, monkeypatch):
     last-tile forms."""
     monkeypatch.setenv("FP8BS_PREFILL_TILE", tile)
     x, w = inputs(M, 1024, 1152, seed=90 + M)
-    check_linear(x, w, f"prefill tile {tile}")
+    # no workspace: the tile shape is not replaced by a split-K schedule
+    check_linear(x, w, f"prefill tile {tile}", workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
 
 
 def test_prefill_default_mid_tile():
     """M = 1024 on the 7168-wide projection: the default schedule picks 128 x 256 tiles."""
     x, w = inputs(1024, 7168, 1024, seed=97)
+    assert fb.workspace_size(1024, 7168, 1024) == 0          # enough tiles: no split
     check_linear(x, w, "prefill 128x256 default")
 
 
@@ -180,7 +182,8 @@ def test_mid_schedules(M, strips, waves, monkeypatch):
     monkeypatch.setenv("FP8BS_MID_STRIPS", strips)
     monkeypatch.setenv("FP8BS_MID_WAVES", waves)
     x, w = inputs(M, 1024, 2176, seed=70 + M)
-    check_linear(x, w, f"mid strips={strips} waves={waves}")
+    check_linear(x, w, f"mid strips={strips} waves={waves}",
+                 workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))    # no split-K: the mid kernel
 
 
 def test_subnormal_codes_and_scales():
@@ -194,6 +197,35 @@ def test_subnormal_codes_and_scales():
     q, s = oracle.quant_act(x)
     assert np.any((q & 0x78) == 0) and np.any(s < np.finfo(np.float32).tiny)
     check_linear(x, w, "subnormal codes")
+
+
+@pytest.mark.parametrize("M,N,K,split", [(65, 1024, 2048, None), (128, 2048, 7168, None), (200, 1024, 4096, None),
+                                         (300, 1152, 2048, None), (128, 1024, 7168, "2"), (100, 512, 3072, "3"),
+                                         (129, 768, 4096, "8"), (80, 256, 512, "4")])
+def test_split_k(M, N, K, split, monkeypatch):
+    """Split-K over the workgroups of each tile (FP32 partials in the workspace, then a
+    fixed-order reduce): within tolerance, and bitwise repeatable."""
+    if split:
+        monkeypatch.setenv("FP8BS_PREFILL_KSPLIT", split)
+    assert fb.workspace_size(M, N, K) > 0 or split
+    x, w = inputs(M, N, K, seed=5 * M + N + K)
+    ws = torch.empty(8 * M * N * 4, dtype=torch.uint8, device="cuda")
+    y = check_linear(x, w, f"split-K {split}", workspace=ws)
+    assert np.array_equal(gpu_path(x, w, workspace=ws), y)
+
+
+def test_split_k_workspace_sizes():
+    """A smaller workspace selects a smaller split or none; every result is in tolerance."""
+    M, N, K = 128, 2048, 4096
+    x, w = inputs(M, N, K, seed=12)
+    ref = oracle_path(x, w)
+    need = fb.workspace_size(M, N, K)
+    assert need > 0
+    for nbytes in (need, need // 2, 2 * M * N * 4, M * N * 4, 0):
+        banner(f"block_linear split-K workspace {nbytes}")
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        res = oracle.check_tolerance(gpu_path(x, w, workspace=ws), ref)
+        assert res["ok"], (nbytes, res)
 
 
 def test_graph_replay_matches_eager():

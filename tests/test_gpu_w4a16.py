@@ -155,6 +155,14 @@ def test_split_k(M, N, K, split, monkeypatch):
     assert_bits_equal(gpu(x, w4, bs, np.float32(2.5e-3), ws), y, "split-K repeat")
 
 
+@pytest.mark.parametrize("M", [17, 25, 32, 33, 48, 63, 64])
+@pytest.mark.parametrize("N,K", [(1024, 1152), (384, 2048)])
+def test_streaming_kernel_without_workspace(M, N, K):
+    """16 < M <= 64 without a workspace runs the streaming kernel (2 or 4 token groups)."""
+    x, w4, bs = random_case(M, N, K, seed=17 * M + N + K)
+    check(x, w4, bs, np.float32(1.0e-3), "streaming", workspace=no_workspace())
+
+
 def test_split_k_workspace_sizes():
     """A smaller workspace selects a smaller split (or none); every result is in
     tolerance and the size query's workspace is enough for the default split."""
