@@ -44,8 +44,8 @@ METRIC = "FP8 block-GEMM TFLOP/s (prefill) and GB/s (decode M=1..8), % of roofli
 KERNEL_SOURCES = {
     "decode": ["gemm_decode.hip", "launch.h", "device_common.h", "api.hip"],
     "mid": ["gemm_mid.hip", "launch.h", "device_common.h", "api.hip"],
-    "prefill": ["gemm_prefill.hip", "launch.h", "device_common.h", "api.hip"],
-    "w4a16": ["w4a16.hip", "launch.h", "device_common.h", "api.hip"],
+    "prefill": ["gemm_prefill.hip", "splitk.hip", "launch.h", "device_common.h", "api.hip"],
+    "w4a16": ["w4a16.hip", "splitk.hip", "launch.h", "device_common.h", "api.hip"],
 }
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
 W4_METRIC = "NVFP4 W4A16 linear: GB/s (decode, M<=64) and TFLOP/s (M>64), % of roofline"
@@ -372,7 +372,10 @@ def load_traffic(path, wl):
 
 
 def _counter_means(directory, name_filter):
-    """{(kernel name, grid): {counter: mean value}} over rocprofv3 counter CSVs."""
+    """{(kernel name, grid): {counter: mean value}} over rocprofv3 counter CSVs, for the
+    kernels whose names contain one of the substrings ``name_filter``."""
+    if isinstance(name_filter, str):
+        name_filter = (name_filter,)
     import csv
     import glob
     from collections import defaultdict
@@ -380,7 +383,7 @@ def _counter_means(directory, name_filter):
     for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
         with open(f) as fh:
             for r in csv.DictReader(fh):
-                if name_filter in r["Kernel_Name"]:
+                if any(f in r["Kernel_Name"] for f in name_filter):
                     acc[(r["Kernel_Name"], r["Grid_Size"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
     return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in acc.items()}
 
@@ -403,7 +406,7 @@ def make_traffic(directory, out_path):
     _, copy_write = one(os.path.join(directory, "copy", "write"), "copyBuffer", "WRITE_SIZE")
     f_fac, w_fac = copy_bytes / (copy_fetch * 1024), copy_bytes / (copy_write * 1024)
     doc = {"method": ("rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, on bench.py --workload W "
-                      "--no-others, kernels matching gemm_ (w4a16_ for the NVFP4 workloads); KiB per "
+                      "--no-others, kernels matching gemm_ (w4a16_ for the NVFP4 workloads) or splitk_reduce; KiB per "
                       "dispatch x 1024 x the factor that maps the same counter onto a 512 MiB device "
                       "copy's bytes"),
            "copy_factor": {"FETCH_SIZE": round(f_fac, 4), "WRITE_SIZE": round(w_fac, 4)},
@@ -413,8 +416,8 @@ def make_traffic(directory, out_path):
         d = os.path.join(directory, name)
         if not os.path.isdir(d):
             continue
-        filt = "w4a16_" if name in W4A16_WORKLOADS else "gemm_"
-        # One call may launch several kernels (the NVFP4 split-K tile and its reduce):
+        filt = ("w4a16_" if name in W4A16_WORKLOADS else "gemm_", "splitk_reduce")
+        # One call may launch several kernels (a split-K tile and its reduce):
         # the call's bytes are the sum over them, the dominant one names the entry.
         fm = _counter_means(os.path.join(d, "fetch"), filt)
         wm = _counter_means(os.path.join(d, "write"), filt)

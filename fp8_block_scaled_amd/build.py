@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8bs.so")
-SOURCES = ["api.hip", "quant.hip", "gemm_decode.hip", "gemm_mid.hip", "gemm_prefill.hip", "w4a16.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm_decode.hip", "gemm_mid.hip", "gemm_prefill.hip", "w4a16.hip", "splitk.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

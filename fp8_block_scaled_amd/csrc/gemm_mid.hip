@@ -183,12 +183,10 @@ template <int R, int NS>
 static hipError_t launch_rns(dim3 grid, dim3 block, unsigned lds, hipStream_t st, const MidArgs& a) {
     // More than 64 KiB of LDS (more waves or token groups) needs the per-kernel limit
     // raised, up to the CU's 160 KiB.
-    static bool attr_set = false;            // idempotent; a race only repeats the call
-    if (lds > 65536 && !attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)gemm_mid_kernel<R, NS>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    static std::atomic<uint64_t> raised{0};
+    if (lds > 65536) {
+        const hipError_t e = raise_lds_limit((const void*)gemm_mid_kernel<R, NS>, raised, 160 * 1024);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     hipLaunchKernelGGL((gemm_mid_kernel<R, NS>), grid, block, lds, st, a);
     return hipSuccess;

@@ -327,12 +327,10 @@ static hipError_t launch_tiles(PrefillArgs a, hipStream_t st) {
     const int64_t T = a.tiles_m * a.tiles_n;
     if (T == 0) return hipSuccess;
     constexpr int lds = prefill_lds_bytes(BM, BN);
-    static bool attr_set = false;          // idempotent; a race only repeats the call
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)gemm_prefill_kernel<BM, BN, WM, WN, CLAMP>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    static std::atomic<uint64_t> raised{0};
+    {
+        const hipError_t e = raise_lds_limit((const void*)gemm_prefill_kernel<BM, BN, WM, WN, CLAMP>, raised, lds);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     hipLaunchKernelGGL((gemm_prefill_kernel<BM, BN, WM, WN, CLAMP>), dim3((unsigned)(T * a.ksplit)),
                        dim3(64 * WM * WN), lds, st, a);

@@ -6,7 +6,24 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fp8bs {
+
+// Raises `fn`'s dynamic-LDS limit to `bytes` on the current device, once per device.
+// hipFuncSetAttribute acts on the current device only, so each launcher keeps one
+// bit per device (devices 0..63; higher ones repeat the idempotent call every time).
+inline hipError_t raise_lds_limit(const void* fn, std::atomic<uint64_t>& done, unsigned bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+    if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return e;
+    done.fetch_or(bit, std::memory_order_relaxed);
+    return hipSuccess;
+}
 
 hipError_t launch_quant_act(const void* x, void* q, float* s, int64_t M, int64_t K, hipStream_t st);
 hipError_t launch_silu_mul_quant(const void* gu, void* q, float* s, int64_t M, int64_t I, hipStream_t st);

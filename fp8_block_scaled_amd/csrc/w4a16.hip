@@ -508,42 +508,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w4a16_tile_kernel(
             }
 }
 
-// Split-K: y = BF16(g * sum over ks of part[ks]) in the order ks = 0, 1, ...; four
-// neighbouring elements per thread (M N is a multiple of 128).  Also used by the FP8
-// prefill GEMM's split-K (g = 1).
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int ksplit, int64_t mn, float g,
-                                                                 uint16_t* y) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= mn) return;
-    v4f sum = *reinterpret_cast<const v4f*>(part + i);
-    for (int ks = 1; ks < ksplit; ++ks) {
-        const v4f v = *reinterpret_cast<const v4f*>(part + (int64_t)ks * mn + i);
-        sum[0] += v[0];
-        sum[1] += v[1];
-        sum[2] += v[2];
-        sum[3] += v[3];
-    }
-    const uint32_t lo = f32_to_bf16_rne(g * sum[0]) | (f32_to_bf16_rne(g * sum[1]) << 16);
-    const uint32_t hi = f32_to_bf16_rne(g * sum[2]) | (f32_to_bf16_rne(g * sum[3]) << 16);
-    *reinterpret_cast<uint2*>(y + i) = make_uint2(lo, hi);
-}
-
-hipError_t launch_splitk_reduce(const float* part, int ksplit, int64_t mn, float g, uint16_t* y, hipStream_t st) {
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, st, part, ksplit, mn,
-                       g, y);
-    return hipGetLastError();
-}
-
 template <int BM, int BN, int WM, int WN, int DEPTH>
 static hipError_t launch_w4_tile(int64_t M, int64_t N, hipStream_t st, const W4Args& a, int ksplit = 1,
                                  float* part = nullptr) {
     constexpr unsigned lds = 2 * (BM * 128 + BN * 32 + BN * 4);
-    static bool attr_set = false;            // idempotent; a race only repeats the call
-    if (lds > 65536 && !attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)w4a16_tile_kernel<BM, BN, WM, WN, DEPTH>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    static std::atomic<uint64_t> raised{0};
+    if (lds > 65536) {
+        const hipError_t e =
+            raise_lds_limit((const void*)w4a16_tile_kernel<BM, BN, WM, WN, DEPTH>, raised, 160 * 1024);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     hipLaunchKernelGGL((w4a16_tile_kernel<BM, BN, WM, WN, DEPTH>), dim3((unsigned)(tiles_m * tiles_n * ksplit)),
@@ -668,12 +641,10 @@ static hipError_t launch_w4_decode_p(const W4Plan& plan, hipStream_t st, const W
 template <int R, int NS>
 static hipError_t launch_w4_rns(dim3 grid, dim3 block, unsigned lds, hipStream_t st, const W4Args& a) {
     // More than 64 KiB of LDS needs the per-kernel limit raised, up to the CU's 160 KiB.
-    static bool attr_set = false;            // idempotent; a race only repeats the call
-    if (lds > 65536 && !attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)w4a16_stream_kernel<R, NS>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    static std::atomic<uint64_t> raised{0};
+    if (lds > 65536) {
+        const hipError_t e = raise_lds_limit((const void*)w4a16_stream_kernel<R, NS>, raised, 160 * 1024);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     hipLaunchKernelGGL((w4a16_stream_kernel<R, NS>), grid, block, lds, st, a);
     return hipSuccess;
