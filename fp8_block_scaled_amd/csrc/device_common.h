@@ -92,22 +92,29 @@ constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
 constexpr int kDppRowMirror = 0x140;      // lane i <-> 15 - i within each 16 lanes
 
-// Max over the 16 lanes of a DPP row; every lane of the row gets the result.
-// Max is exact and order-independent, so the result is bit-exact.
+// Max over the 16 lanes of a DPP row of non-negative values (group amaxes); every
+// lane of the row gets the result.  Non-negative floats order as their bit
+// patterns, so the max is taken on the integers: exact, order-independent, and
+// without the NaN canonicalization a float max would add per step.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
 __device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
-    v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
-    v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
-    v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
-    return v;
+    uint32_t u = __float_as_uint(v);
+    u = max(u, dpp_u32<kDppQuadXor1>(u));
+    u = max(u, dpp_u32<kDppQuadXor2>(u));
+    u = max(u, dpp_u32<kDppRowHalfMirror>(u));
+    u = max(u, dpp_u32<kDppRowMirror>(u));
+    return __uint_as_float(u);
 }
 
-// Max over a full wave of 64 lanes.
+// Max over a full wave of 64 lanes (non-negative values).
 __device__ __forceinline__ float wave_max(float v) {
-    v = row16_max(v);
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    uint32_t u = __float_as_uint(row16_max(v));
+    u = max(u, (uint32_t)__shfl_xor((int)u, 16));
+    u = max(u, (uint32_t)__shfl_xor((int)u, 32));
+    return __uint_as_float(u);
 }
 
 }  // namespace fp8bs

@@ -164,48 +164,72 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(
 //   1. it loads those chunks of x and gamma (kept in registers when the row fits,
 //      U chunks per thread) and sums the squares of x in float64 (x^2 is exact for
 //      BF16 x); the wave (shuffles) and the workgroup (LDS, fixed order, so the
-//      result is deterministic) reduce;  r = 1 / sqrt(sum / K + eps);
+//      result is deterministic) reduce;  r = 1 / sqrt(sum / K + eps) (rsqrt_f64);
 //   2. per group: h = BF16((x r) gamma), the BF16 rounding of the float64 value
 //      (decided in float32 where that is provably the same), then the group's
 //      amax, scale and codes as in quant_act_kernel.
 // U = 0 is the general form for long rows: x and gamma are read again in step 2
 // (from cache).
 constexpr int kNormThreads = 256;
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr int kNormRowsPerPass = kNormThreads / 16;      // groups in flight per pass
 
 // h = BF16((x r) gamma) for 8 values, exactly rounded.  Float32 first:
 // h32 = fl32(fl32(x r32) gamma) is within 4 float32 ulps of the exact product, so its
-// BF16 rounding is the exact one unless h32 lies within 8 ulps of a BF16 rounding
-// midpoint (low 16 bits near 0x8000) or in the BF16 subnormal range; those
-// elements (rare) are redone in float64.
+// BF16 rounding (v_cvt_pk_bf16_f32, nearest even) is the exact one unless h32 lies
+// within 8 ulps of a BF16 rounding midpoint (low 16 bits in [0x7FF8, 0x8008)) or
+// below 2^-120 in magnitude (near the BF16 subnormal range); those elements (rare)
+// are redone in float64.
 __device__ __forceinline__ void rmsnorm8(const float (&xf)[8], const float (&gf)[8], double r, float r32,
                                          float (&h)[8]) {
-    uint32_t hb[8];
-    bool redo = false;
+    float h32[8];
+    // The tests are collected as wave masks (one compare each, the masks combined
+    // by scalar instructions), not as per-lane booleans.
+    uint64_t redo_mask = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float h32 = (xf[i] * r32) * gf[i];
-        const uint32_t b = __float_as_uint(h32);
-        const uint32_t a = b & 0x7FFFFFFFu;
-        hb[i] = f32_to_bf16_rne(h32);
-        redo |= ((b & 0xFFFFu) - 0x7FF8u) < 0x10u || (a != 0u && a < 0x03800000u);
+        h32[i] = (xf[i] * r32) * gf[i];
+        const uint32_t b = __float_as_uint(h32[i]);
+        redo_mask |= __builtin_amdgcn_ballot_w64(((b + 8u) & 0xFFF0u) == 0x8000u);
+        redo_mask |= __builtin_amdgcn_ballot_w64(fabsf(h32[i]) < 0x1p-120f) &
+                     __builtin_amdgcn_ballot_w64(h32[i] != 0.0f);
     }
-    if (redo) {
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        const v2f pair = {h32[i], h32[i + 1]};
+        const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, v2bf));
+        h[i] = __uint_as_float(hb << 16);
+        h[i + 1] = __uint_as_float(hb & 0xFFFF0000u);
+    }
+    if (redo_mask) {                                   // wave-uniform; lanes re-test their elements
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint32_t b = __float_as_uint((xf[i] * r32) * gf[i]);
-            const uint32_t a = b & 0x7FFFFFFFu;
-            if (((b & 0xFFFFu) - 0x7FF8u) < 0x10u || (a != 0u && a < 0x03800000u))
-                hb[i] = f64_to_bf16_rne(((double)xf[i] * r) * (double)gf[i]);
+            const uint32_t b = __float_as_uint(h32[i]);
+            if (((b + 8u) & 0xFFF0u) == 0x8000u || (fabsf(h32[i]) < 0x1p-120f && h32[i] != 0.0f))
+                h[i] = bf16_to_f32(f64_to_bf16_rne(((double)xf[i] * r) * (double)gf[i]));
         }
     }
+}
+
+// 1 / sqrt(a) for a > 0, a normal float64: the hardware estimate and three Newton
+// steps y <- y + y (1/2 - (a/2) y^2), each at least squaring the relative error, so
+// the result is within a few float64 ulps (the BF16 rounding of h needs about
+// 2^-40; the FP64 redo of a near-midpoint element sees the same few-ulp r).
+__device__ __forceinline__ double rsqrt_f64(double a) {
+    const double half_a = 0.5 * a;
+    double y = __builtin_amdgcn_rsq(a);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = bf16_to_f32(hb[i]);
+    for (int it = 0; it < 3; ++it) {
+        const double e = fma(-half_a * y, y, 0.5);
+        y = fma(y, e, y);
+    }
+    return y;
 }
 
 template <int U>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, double eps, uint8_t* __restrict__ q,
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, double eps, double inv_k, uint8_t* __restrict__ q,
     float* __restrict__ s, int64_t K) {
     __shared__ double part[kNormThreads / 64];
     const int64_t m = blockIdx.x;
@@ -250,7 +274,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
     double total = 0.0;
 #pragma unroll
     for (int w = 0; w < kNormThreads / 64; ++w) total += part[w];
-    const double r = 1.0 / sqrt(total / (double)K + eps);
+    const double r = rsqrt_f64(total * inv_k + eps);
     const float r32 = (float)r;
 
     auto emit = [&](int64_t j, const uint4& xv, const uint4& gv) {      // uniform over the 16-lane row
@@ -284,18 +308,19 @@ hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, float eps, voi
     const uint16_t* xp = (const uint16_t*)x;
     const uint16_t* gp = (const uint16_t*)gamma;
     const double e = (double)eps;
+    const double inv_k = 1.0 / (double)K;
     if (passes <= 1)
-        hipLaunchKernelGGL(rmsnorm_quant_kernel<1>, grid, block, 0, st, xp, gp, e, (uint8_t*)q, s, K);
+        hipLaunchKernelGGL(rmsnorm_quant_kernel<1>, grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
     else if (passes <= 2)
-        hipLaunchKernelGGL(rmsnorm_quant_kernel<2>, grid, block, 0, st, xp, gp, e, (uint8_t*)q, s, K);
+        hipLaunchKernelGGL(rmsnorm_quant_kernel<2>, grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
     else if (passes <= 4)
-        hipLaunchKernelGGL(rmsnorm_quant_kernel<4>, grid, block, 0, st, xp, gp, e, (uint8_t*)q, s, K);
+        hipLaunchKernelGGL(rmsnorm_quant_kernel<4>, grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
     else if (passes <= 8)
-        hipLaunchKernelGGL(rmsnorm_quant_kernel<8>, grid, block, 0, st, xp, gp, e, (uint8_t*)q, s, K);
+        hipLaunchKernelGGL(rmsnorm_quant_kernel<8>, grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
     else if (passes <= 16)
-        hipLaunchKernelGGL(rmsnorm_quant_kernel<16>, grid, block, 0, st, xp, gp, e, (uint8_t*)q, s, K);
+        hipLaunchKernelGGL(rmsnorm_quant_kernel<16>, grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
     else
-        hipLaunchKernelGGL(rmsnorm_quant_kernel<0>, grid, block, 0, st, xp, gp, e, (uint8_t*)q, s, K);
+        hipLaunchKernelGGL(rmsnorm_quant_kernel<0>, grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
     return hipGetLastError();
 }
 

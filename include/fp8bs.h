@@ -95,8 +95,8 @@ int fp8_silu_mul_quant(const void* gu_bf16, void* q_e4m3, float* s_f32,
  *   q_e4m3     [M, K]      E4M3 codes of h (out).
  *   s_f32      [M, K/128]  scales of h (out).
  * h[m, k] = x[m, k] / sqrt(mean_k x[m, k]^2 + eps) * gamma[k], evaluated in FP64
- * (eps widened exactly) and rounded to BF16 once (nearest even).  K must be a
- * multiple of 128.  Deterministic.
+ * (eps widened exactly; the reciprocal square root within a few FP64 ulps) and
+ * rounded to BF16 once (nearest even).  K must be a multiple of 128.  Deterministic.
  */
 int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, float eps,
                       void* q_e4m3, float* s_f32, int64_t M, int64_t K, hipStream_t stream);
