@@ -65,7 +65,8 @@ const char* fp8bs_status_string(int status) {
         case FP8BS_ERR_DEVICE: return "the current HIP device is not gfx950 (MI355X)";
         case FP8BS_ERR_HIP: return "HIP runtime call or kernel launch failed";
         case FP8BS_ERR_WORKSPACE: return "workspace must be 256-byte aligned";
-        case FP8BS_ERR_VALUE: return "scalar argument out of range (eps must be finite and > 0)";
+        case FP8BS_ERR_VALUE:
+            return "scalar argument out of range (RMSNorm eps must be finite and > 0, the NVFP4 global scale finite)";
         default: return "unknown fp8bs status";
     }
 }

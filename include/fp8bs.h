@@ -44,7 +44,7 @@ typedef enum {
     FP8BS_ERR_DEVICE = -4,    /* the current device is not gfx950                 */
     FP8BS_ERR_HIP = -5,       /* a HIP runtime call or a kernel launch failed     */
     FP8BS_ERR_WORKSPACE = -6, /* workspace given but misaligned                   */
-    FP8BS_ERR_VALUE = -7      /* a scalar argument out of range (eps <= 0, NaN g) */
+    FP8BS_ERR_VALUE = -7      /* a scalar argument out of range (eps <= 0, non-finite g) */
 } fp8bs_status;
 
 /*
