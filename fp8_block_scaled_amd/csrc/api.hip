@@ -132,7 +132,7 @@ int fp8_block_linear(const void* q_e4m3, const float* s_f32, const void* w_e4m3,
         return hip_status(
             fp8bs::launch_gemm_decode(plan, q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, stream));
     }
-    // 24 < M <= 64 with a workspace: split-K tiles beat weight streaming.
+    // 32 < M <= 64 with a workspace: split-K tiles beat weight streaming.
     if (M <= fp8bs::kMidMaxM &&
         !(M > fp8bs::kSplitMinM && workspace && fp8bs::prefill_plan_split(M, N, K, cus, workspace_bytes) >= 2)) {
         const fp8bs::MidPlan plan = fp8bs::plan_mid(M, N, K, cus);

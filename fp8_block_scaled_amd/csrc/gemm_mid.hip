@@ -164,11 +164,29 @@ MidPlan plan_mid(int64_t M, int64_t N, int64_t K, int cus) {
     p.groups = M <= 32 ? 2 : (M <= 64 ? 4 : 8);          // 8 only through kMidMaxM changes
     p.strips = N / 16;
     p.kblocks = K / kGroup;
-    // Two strips per workgroup once that still leaves two workgroups per CU.
-    p.strips_per_wg = (p.groups <= 4 && p.strips >= 4 * (int64_t)cus) ? 2 : 1;
-    if (const char* e = getenv("FP8BS_MID_STRIPS")) {       // tuning hook (2 only with R <= 4)
+    // Strips per workgroup: every workgroup reads all 16 R activation rows (from L2)
+    // plus 16 weight rows per strip, and a CU holds several workgroups at once, so the
+    // busiest CU moves ceil(workgroups / CUs) (16 R + 16 NS) K bytes.  NS minimizes
+    // that (ties to the larger NS: less L2 traffic in total).  Measured at K = 7168,
+    // M = 17 .. 32: N = 7168 takes NS = 2 (16.3 .. 19.9 us, against 21 .. 28 with one
+    // strip), N = 9216 and 16384 take NS = 4 (23 .. 29 us, against 30 .. 53).
+    // NS = 4 only with R = 2 (registers), NS = 2 with R <= 4.
+    {
+        const int max_ns = p.groups <= 2 ? 4 : (p.groups <= 4 ? 2 : 1);
+        int64_t best = -1;
+        for (int ns = 1; ns <= max_ns; ns *= 2) {
+            const int64_t wgs = (p.strips + ns - 1) / ns;
+            const int64_t per_cu = (wgs + cus - 1) / cus;
+            const int64_t bytes = per_cu * (p.groups + ns);
+            if (best < 0 || bytes <= best) {
+                best = bytes;
+                p.strips_per_wg = ns;
+            }
+        }
+    }
+    if (const char* e = getenv("FP8BS_MID_STRIPS")) {       // tuning hook (4 only with R = 2, 2 with R <= 4)
         const int v = atoi(e);
-        if (v == 1 || (v == 2 && p.groups <= 4)) p.strips_per_wg = v;
+        if (v == 1 || (v == 2 && p.groups <= 4) || (v == 4 && p.groups <= 2)) p.strips_per_wg = v;
     }
     p.workgroups = (p.strips + p.strips_per_wg - 1) / p.strips_per_wg;
     p.waves = (int)(p.kblocks < kMidWaves ? p.kblocks : kMidWaves);
@@ -195,6 +213,7 @@ static hipError_t launch_rns(dim3 grid, dim3 block, unsigned lds, hipStream_t st
 template <int R>
 static hipError_t launch_r(const MidPlan& plan, dim3 grid, dim3 block, unsigned lds, hipStream_t st,
                            const MidArgs& a) {
+    if (R <= 2 && plan.strips_per_wg == 4) return launch_rns<R, R <= 2 ? 4 : 1>(grid, block, lds, st, a);
     if (R <= 4 && plan.strips_per_wg == 2) return launch_rns<R, R <= 4 ? 2 : 1>(grid, block, lds, st, a);
     return launch_rns<R, 1>(grid, block, lds, st, a);
 }

@@ -348,7 +348,8 @@ static hipError_t launch_shape(PrefillArgs a, hipStream_t st) {
 // Split-K ways for a shape whose 128 x 128 tiles leave CUs idle (0: none); the
 // workspace size query assumes up to 256 CUs.  Above kSplitMinM rows split-K tiles
 // beat the weight-streaming mid-size kernel (measured on the 7168 x 7168
-// projection: 25.0 against 28.7 us at M = 32, 26.7 against 49.6 us at M = 64).
+// projection: 25.0 against 26.2 us at M = 48, 25.7 against 30.0 us at M = 64; at
+// M <= 32 the mid-size kernel is faster: 19.9 against 24.6 us at M = 32).
 int prefill_split(int64_t M, int64_t N, int64_t K, int cus) {
     if (M <= kSplitMinM) return 0;
     const int64_t t = (M + 127) / 128 * (N / 128);

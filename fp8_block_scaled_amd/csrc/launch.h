@@ -52,7 +52,7 @@ hipError_t launch_gemm_decode(const DecodePlan& plan, const void* q, const float
 // (above 64 rows the 128 x 128 prefill tiles are faster)
 constexpr int kMidMaxM = 64;
 // Above this many rows a split-K prefill schedule (given a workspace) is used instead.
-constexpr int kSplitMinM = 24;
+constexpr int kSplitMinM = 32;
 
 struct MidPlan {
     int groups;          // R: 16-token groups per weight fragment (2, 4 or 8)

@@ -108,7 +108,7 @@ int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, float eps,
  *   y_bf16  [M, N]            output (out), rounded to BF16 (nearest even) once.
  *   workspace / workspace_bytes
  *       Optional device scratch, sized by fp8_block_linear_workspace_size.  With it,
- *       a batch too small to give every CU a tile (64 < M up to a few hundred tokens)
+ *       a batch too small to give every CU a tile (32 < M up to a few hundred tokens)
  *       splits K over the workgroups of each tile: FP32 partial sums go to the
  *       workspace and a second kernel adds them in a fixed order.  NULL / 0, or a
  *       smaller workspace, selects a schedule that fits (never an error); it must be
@@ -126,8 +126,8 @@ int fp8_block_linear(const void* q_e4m3, const float* s_f32,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace the fastest schedule of fp8_block_linear can use for this shape
- * on devices of up to 256 CUs (0 if none: decode and mid-size shapes, and prefill
- * shapes with enough tiles; 0 for invalid shapes as well). */
+ * on devices of up to 256 CUs (0 if none: M <= 32, and prefill shapes with enough
+ * tiles; 0 for invalid shapes as well). */
 size_t fp8_block_linear_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*

@@ -137,9 +137,9 @@ def test_valid_call_without_a_gpu_reports_a_hip_error_not_a_crash(L):
 
 def test_workspace_size_query(L):
     for shape in ((8191, 7168, 7168), (4, 100, 128), (-1, 128, 128), (1, 9216, 7168), (8, 7168, 8192),
-                  (24, 7168, 7168), (2048, 7168, 7168)):
+                  (24, 7168, 7168), (32, 7168, 7168), (2048, 7168, 7168)):
         assert L.fp8_block_linear_workspace_size(*shape) == 0
-    assert L.fp8_block_linear_workspace_size(25, 7168, 7168) == 4 * 25 * 7168 * 4   # split-K above 24 rows
+    assert L.fp8_block_linear_workspace_size(33, 7168, 7168) == 4 * 33 * 7168 * 4   # split-K above 32 rows
     # 56 tiles of 128 x 128: split 4 (256 / 56), FP32 [4][M][N]
     assert L.fp8_block_linear_workspace_size(128, 7168, 7168) == 4 * 128 * 7168 * 4
     # capped at 8 ways and at a quarter of the K blocks

@@ -175,15 +175,31 @@ def test_prefill_default_mid_tile():
     check_linear(x, w, "prefill 128x256 default")
 
 
-@pytest.mark.parametrize("M", [17, 40, 64])
-@pytest.mark.parametrize("strips,waves", [("1", "8"), ("2", "8"), ("1", "3"), ("2", "5")])
+@pytest.mark.parametrize("M", [17, 32, 40, 64])
+@pytest.mark.parametrize("strips,waves", [("1", "8"), ("2", "8"), ("4", "8"), ("1", "3"), ("2", "5"), ("4", "6")])
 def test_mid_schedules(M, strips, waves, monkeypatch):
-    """The mid-size kernel (16 < M <= 64) under every strip count and several split-K degrees."""
+    """The mid-size kernel (16 < M <= 64) under every strip count (4 only up to 32 rows;
+    the hook leaves larger M on its own choice) and several in-workgroup split-K degrees."""
     monkeypatch.setenv("FP8BS_MID_STRIPS", strips)
     monkeypatch.setenv("FP8BS_MID_WAVES", waves)
     x, w = inputs(M, 1024, 2176, seed=70 + M)
     check_linear(x, w, f"mid strips={strips} waves={waves}",
                  workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))    # no split-K: the mid kernel
+
+
+@pytest.mark.parametrize("M,N,K", [(20, 9216, 512), (32, 16384, 256), (30, 7168, 384), (48, 9216, 256),
+                                   (25, 1024, 1024)])
+def test_mid_default_plans(M, N, K):
+    """The mid-size kernel's own strip choice (4 strips per workgroup on wide N up to 32
+    rows, 2 on N = 7168, 1 on narrow N), with and without a workspace: M <= 32 stays on
+    this kernel even when a workspace is given."""
+    x, w = inputs(M, N, K, seed=3 * M + N)
+    y = check_linear(x, w, "mid default plan", workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    ws = torch.empty(8 * M * N * 4, dtype=torch.uint8, device="cuda")
+    if M <= 32:
+        assert np.array_equal(gpu_path(x, w, workspace=ws), y)
+    else:
+        check_linear(x, w, "mid-size M with a workspace", workspace=ws)
 
 
 def test_subnormal_codes_and_scales():

@@ -166,6 +166,23 @@ def test_rmsnorm_quant_random(M, K):
     check_rmsnorm(x, g, np.float32(1e-5), "random")
 
 
+def test_rmsnorm_quant_redo_path():
+    """Inputs with many elements whose float32 product x r gamma lies within 8 ulps of a
+    BF16 rounding midpoint, the case the kernel recomputes in float64: the count is
+    taken on the host first, so the test is known to reach that path."""
+    rng = np.random.default_rng(41)
+    M, K = 512, 2048
+    x = bf16(rng.standard_normal((M, K)))
+    g = bf16(rng.standard_normal(K) * 0.3 + 1.0)
+    xf = oracle.bf16_bits_to_f32(x).astype(np.float64)
+    r = 1.0 / np.sqrt(np.mean(xf * xf, axis=1, keepdims=True) + 1e-5)
+    h32 = (oracle.bf16_bits_to_f32(x) * r.astype(np.float32)) * oracle.bf16_bits_to_f32(g)
+    low = h32.astype(np.float32).view(np.uint32) & 0xFFFF
+    near = int(np.count_nonzero((low >= 0x7FF8) & (low < 0x8008)))
+    assert near > 100, near
+    check_rmsnorm(x, g, np.float32(1e-5), f"{near} near-midpoint elements")
+
+
 def test_rmsnorm_quant_edge_rows():
     rng = np.random.default_rng(3)
     K = 1024
