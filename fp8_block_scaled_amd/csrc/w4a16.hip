@@ -52,9 +52,10 @@ typedef float v8f __attribute__((ext_vector_type(8)));
 constexpr int kW4MaxWaves = 8;
 constexpr int64_t kW4StreamMaxM = 64;      // above: LDS-tiled kernel
 // Above this many rows split-K tiles (given a workspace) beat the streaming kernel
-// (measured on the 7168 x 7168 projection: 31.9 against 35.4 us at M = 32, 34.5
-// against 71.0 us at M = 64).
-constexpr int64_t kW4SplitMinM = 24;
+// (measured at K = 7168, N = 7168 / 9216 / 16384: 31.9 / 35.7 / 48.8 against
+// 34.9 / 64.1 / 67.7 us at M = 40; up to 32 rows the streaming kernel wins: 23.6 /
+// 31.7 / 33.5 against 31.4 / 34.0 / 47.5 us at M = 32).
+constexpr int64_t kW4SplitMinM = 32;
 constexpr int64_t kW4MaxSplit = 8;         // split-K ways at most
 
 struct W4Args {
@@ -544,10 +545,26 @@ W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus, size_t workspace_byt
     p.strips = N / 16;
     p.kblocks = K / kGroup;
     p.m_chunks = M > 0 ? (M + 16 * p.groups - 1) / (16 * p.groups) : 0;
-    p.strips_per_wg = (p.strips >= 4 * (int64_t)cus) ? 2 : 1;
+    // Strips per workgroup of the streaming kernel: every workgroup reads its 16 R
+    // BF16 activation rows (from L2) and, per strip, 16 rows of codes and scales
+    // (K / 2 + K / 16 bytes each), and a CU runs several workgroups at once, so the
+    // busiest CU moves ceil(workgroups / CUs) (32 R + 9 NS) K bytes; NS minimizes that
+    // (ties to the larger NS).  NS = 4 only with R <= 2 (registers).
+    {
+        const int max_ns = p.groups <= 2 ? 4 : 2;
+        int64_t best = -1;
+        for (int ns = 1; ns <= max_ns; ns *= 2) {
+            const int64_t wgs = (p.strips + ns - 1) / ns;
+            const int64_t bytes = ((wgs + cus - 1) / cus) * (32 * (int64_t)p.groups + 9 * ns);
+            if (best < 0 || bytes <= best) {
+                best = bytes;
+                p.strips_per_wg = ns;
+            }
+        }
+    }
     if (const char* e = getenv("FP8BS_W4_STRIPS")) {        // tuning hook
         const int v = atoi(e);
-        if (v == 1 || v == 2) p.strips_per_wg = v;
+        if (v == 1 || v == 2 || (v == 4 && p.groups <= 2)) p.strips_per_wg = v;
     }
     p.strip_wgs = (p.strips + p.strips_per_wg - 1) / p.strips_per_wg;
     p.waves = (int)(p.kblocks < kW4MaxWaves ? p.kblocks : kW4MaxWaves);
@@ -556,7 +573,7 @@ W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus, size_t workspace_byt
         if (v >= 1 && v <= kW4MaxWaves) p.waves = v;
     }
     // M > 64: LDS-tiled kernel, the largest tile that still gives (nearly) every CU
-    // a workgroup; 24 < M <= 64 too when a split-K schedule fits the workspace.
+    // a workgroup; 32 < M <= 64 too when a split-K schedule fits the workspace.
     const int64_t t2s = ((M + 127) / 128) * ((N + 255) / 256);
     const bool small_split = M > kW4SplitMinM && M <= kW4StreamMaxM && t2s < cus - cus / 8 &&
                              (K / kW4TileK) / 2 >= 2 &&
@@ -653,6 +670,7 @@ static hipError_t launch_w4_rns(dim3 grid, dim3 block, unsigned lds, hipStream_t
 template <int R>
 static hipError_t launch_w4_r(const W4Plan& plan, dim3 grid, dim3 block, unsigned lds, hipStream_t st,
                               const W4Args& a) {
+    if (R <= 2 && plan.strips_per_wg == 4) return launch_w4_rns<R, R <= 2 ? 4 : 1>(grid, block, lds, st, a);
     if (plan.strips_per_wg == 2) return launch_w4_rns<R, 2>(grid, block, lds, st, a);
     return launch_w4_rns<R, 1>(grid, block, lds, st, a);
 }

@@ -117,8 +117,9 @@ def test_nvfp4_linear_validation(L):
 
 def test_nvfp4_workspace_size_query(L):
     q = L.nvfp4_w4a16_workspace_size
-    assert q(1, 9216, 7168) == 0 and q(16, 7168, 8192) == 0 and q(24, 7168, 7168) == 0    # decode / streaming
-    assert q(64, 7168, 7168) == 8 * 64 * 7168 * 4                        # split-K tiles above 24 rows
+    assert q(1, 9216, 7168) == 0 and q(16, 7168, 8192) == 0 and q(32, 7168, 7168) == 0    # decode / streaming
+    assert q(64, 7168, 7168) == 8 * 64 * 7168 * 4                        # split-K tiles above 32 rows
+    assert q(33, 7168, 7168) == 8 * 33 * 7168 * 4
     assert q(2048, 7168, 7168) == 0                                      # enough tiles without a split
     assert q(128, 16384, 7168) == 4 * 128 * 16384 * 4                     # 64 tiles: split 4
     assert q(100, 1024, 1152) == 8 * 100 * 1024 * 4                       # split capped at 8 ...

@@ -163,6 +163,21 @@ def test_streaming_kernel_without_workspace(M, N, K):
     check(x, w4, bs, np.float32(1.0e-3), "streaming", workspace=no_workspace())
 
 
+@pytest.mark.parametrize("M,N,K,strips", [(20, 1024, 1152, "4"), (32, 384, 2048, "4"), (30, 1024, 1152, "2"),
+                                          (17, 9216, 512, None), (32, 16384, 256, None), (25, 7168, 384, None),
+                                          (40, 9216, 256, None), (64, 1024, 1152, "2")])
+def test_streaming_strips(M, N, K, strips, monkeypatch):
+    """The streaming kernel with 1, 2 or 4 strips per workgroup (forced, or the host's own
+    choice on wide N); M <= 32 streams even with a workspace."""
+    if strips:
+        monkeypatch.setenv("FP8BS_W4_STRIPS", strips)
+    x, w4, bs = random_case(M, N, K, seed=29 * M + N + K)
+    y = check(x, w4, bs, np.float32(1.0e-3), f"streaming strips={strips}", workspace=no_workspace())
+    if M <= 32:
+        ws = torch.empty(8 * M * N * 4, dtype=torch.uint8, device="cuda")
+        assert_bits_equal(gpu(x, w4, bs, np.float32(1.0e-3), ws), y, "with a workspace: the same schedule")
+
+
 def test_split_k_workspace_sizes():
     """A smaller workspace selects a smaller split (or none); every result is in
     tolerance and the size query's workspace is enough for the default split."""
