@@ -391,18 +391,30 @@ hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, con
     a.KB = K / kGroup;
     a.ksplit = 1;
     a.part = nullptr;
-    // Tile shape, 8 waves each: the largest of 256 x 256 (waves of 64 x 128),
-    // 128 x 256 and 128 x 128 that still gives nearly every CU a tile (measured on
-    // M = 129 .. 8191, N = K = 7168: a tile row of 256 wins only when there are
-    // enough tiles to fill the GPU).  Tuning hook FP8BS_PREFILL_TILE = 256256,
-    // 256128, 128256 or 128128 forces a shape.
+    // Tile shape, 8 waves each.  A CU runs one tile at a time, so a call takes
+    // ceil(tiles / CUs) rounds of one tile's time; the tile times per round measured
+    // at N = K = 7168 with every CU busy are 107 (256 x 256, waves of 64 x 128),
+    // 76 (128 x 256) and 57 us (128 x 128), i.e. relative costs 187 : 133 : 100.
+    // The shape with the least rounds x cost wins (measured: M = 768 takes 128 x 256,
+    // 74 against 98 us with 128 x 128 tiles; M = 1536 takes 256 x 256, 98 against
+    // 138 us with 128 x 256).  N not a multiple of 256: the largest of 256 x 128 and
+    // 128 x 128 that still gives nearly every CU a tile.  Tuning hook
+    // FP8BS_PREFILL_TILE = 256256, 256128, 128256 or 128128 forces a shape.
     const bool n256 = N % 256 == 0;
     const int64_t enough = cus - cus / 8;
     auto tiles = [&](int64_t bm, int64_t bn) { return (M + bm - 1) / bm * (N / bn); };
+    auto rounds = [&](int64_t t) { return (t + cus - 1) / cus; };
     int tile = 128128;
-    if (n256 && tiles(256, 256) >= enough) tile = 256256;
-    else if (n256 && tiles(128, 256) >= enough) tile = 128256;
-    else if (!n256 && tiles(256, 128) >= enough) tile = 256128;
+    if (n256) {
+        int64_t best = rounds(tiles(128, 128)) * 100;
+        if (rounds(tiles(128, 256)) * 133 < best) {
+            best = rounds(tiles(128, 256)) * 133;
+            tile = 128256;
+        }
+        if (rounds(tiles(256, 256)) * 187 < best) tile = 256256;
+    } else if (tiles(256, 128) >= enough) {
+        tile = 256128;
+    }
     if (const char* e = getenv("FP8BS_PREFILL_TILE")) {
         const int t = atoi(e);
         if (t == 256128 || t == 128128 || (n256 && (t == 256256 || t == 128256))) tile = t;
