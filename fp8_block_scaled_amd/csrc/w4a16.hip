@@ -581,10 +581,22 @@ W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus, size_t workspace_byt
     if (M > kW4StreamMaxM || small_split) {
         const int64_t enough = cus - cus / 8;
         auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-        if (tiles(256, 256) >= enough) p.tile = 256256;
-        else if (tiles(128, 256) >= enough) p.tile = 128256;
-        else if (tiles(128, 128) >= enough) p.tile = 128128;
-        else p.tile = 64128;
+        // A CU runs one tile at a time, so a call takes ceil(tiles / CUs) rounds; one
+        // round with every CU busy takes 75 (64 x 128), 94 (128 x 128), 150 (128 x 256)
+        // and 221 us (256 x 256) at N = K = 7168.  The shape with the least rounds x
+        // round time wins (measured: M = 768 on N = 7168 takes 128 x 256, 149 against
+        // 184 us; M = 1536 takes 256 x 256, 208 against 290 us).
+        {
+            const int shapes[4][3] = {{64, 128, 75}, {128, 128, 94}, {128, 256, 150}, {256, 256, 221}};
+            int64_t best = -1;
+            for (const auto& sh : shapes) {
+                const int64_t cost = ((tiles(sh[0], sh[1]) + cus - 1) / cus) * sh[2];
+                if (best < 0 || cost < best) {
+                    best = cost;
+                    p.tile = sh[0] * 1000 + sh[1];
+                }
+            }
+        }
         if (const char* e = getenv("FP8BS_W4_TILE")) {       // tuning hook
             const int v = atoi(e);
             if (v == 256256 || v == 128256 || v == 128128 || v == 64128) p.tile = v;
