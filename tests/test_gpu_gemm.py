@@ -202,6 +202,29 @@ def test_mid_default_plans(M, N, K):
         check_linear(x, w, "mid-size M with a workspace", workspace=ws)
 
 
+def _random_shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        M = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 65)), int(rng.integers(65, 1200))]))
+        N = 128 * int(rng.integers(1, 40))
+        K = 128 * int(rng.integers(1, 12))
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_shapes(2024, 24))
+def test_linear_random_shapes(M, N, K):
+    """Seeded random shapes across every schedule the host can pick (decode, mid-size
+    strips, split-K, each tile shape), with the binding's default workspace and without."""
+    x, w = inputs(M, N, K, seed=M + 7 * N + 13 * K)
+    ref = oracle_path(x, w)
+    for ws in (None, torch.empty(0, dtype=torch.uint8, device="cuda")):
+        banner(f"block_linear random shape M={M} N={N} K={K} workspace={'default' if ws is None else 'none'}")
+        res = oracle.check_tolerance(gpu_path(x, w, workspace=ws), ref)
+        assert res["ok"], res
+
+
 def test_subnormal_codes_and_scales():
     """E4M3 subnormal codes and FP32-subnormal scales reach the MFMA and the promotion."""
     rng = np.random.default_rng(13)

@@ -178,6 +178,29 @@ def test_streaming_strips(M, N, K, strips, monkeypatch):
         assert_bits_equal(gpu(x, w4, bs, np.float32(1.0e-3), ws), y, "with a workspace: the same schedule")
 
 
+def _random_shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        M = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 65)), int(rng.integers(65, 1200))]))
+        N = 128 * int(rng.integers(1, 40))
+        K = 128 * int(rng.integers(1, 12))
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_shapes(2025, 24))
+def test_random_shapes(M, N, K):
+    """Seeded random shapes across every schedule the host can pick (decode, streaming
+    strips, split-K, each tile shape), with the binding's default workspace and without."""
+    x, w4, bs = random_case(M, N, K, seed=M + 5 * N + 11 * K)
+    ref = oracle.linear_w4a16_ref(x, w4, bs, np.float32(1e-3))
+    for ws in (None, no_workspace()):
+        banner(f"nvfp4_linear random shape M={M} N={N} K={K} workspace={'default' if ws is None else 'none'}")
+        res = oracle.check_tolerance(gpu(x, w4, bs, np.float32(1e-3), ws), ref)
+        assert res["ok"], res
+
+
 def test_split_k_workspace_sizes():
     """A smaller workspace selects a smaller split (or none); every result is in
     tolerance and the size query's workspace is enough for the default split."""
