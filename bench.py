@@ -228,6 +228,34 @@ def time_rmsnorm_quant(wl, steps):
                          "frac": round(achieved / HBM_PEAK_GBS, 4)}}
 
 
+def time_silu_mul_quant(M, I, steps):
+    """Average duration of fp8_silu_mul_quant on [gate | up] BF16 [M, 2I] ~ N(0, 1.7^2)
+    (the gate/up GEMM's output scale) and its HBM roofline: read gate and up, write
+    codes and scales."""
+    import numpy as np
+    import torch
+    import fp8_block_scaled_amd as fb
+    import synth
+    gu = torch.from_numpy(synth.bf16_normal(M, 2 * I, 1.7, 0, synth.TID_GU).view(np.int16)).cuda()
+    q = torch.empty((M, I), dtype=torch.uint8, device="cuda")
+    s = torch.empty((M, I // 128), dtype=torch.float32, device="cuda")
+    gu = gu.view(torch.bfloat16)
+    for _ in range(3):
+        fb.silu_mul_quant(gu, q, s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            fb.silu_mul_quant(gu, q, s)
+    graph.replay()
+    us = _replay_ms(graph) * 1e3 / steps
+    nbytes = 4 * M * I + M * I + 4 * M * (I // 128)
+    achieved = nbytes / (us * 1e-6) / 1e9
+    return {"M": M, "I": I, "us": round(us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4)}}
+
+
 def time_m_sweep(Ms=(32, 64, 128, 512, 2048), N=7168, K=7168, copies=8, steps=40):
     """block_linear on the o_proj shape (N = K = 7168) for row counts between the
     decode and the prefill workloads: batched decode and chunked prefill.  Weights
@@ -607,6 +635,9 @@ def main():
         print("[bench] rmsnorm_quant", file=sys.stderr, flush=True)
         out["rmsnorm_quant"] = {name: time_rmsnorm_quant(WORKLOADS[name], 50 if name == "prefill_oproj" else 200)
                                 for name in ("decode_qkv", "prefill_oproj")}
+        print("[bench] silu_mul_quant", file=sys.stderr, flush=True)
+        out["silu_mul_quant"] = {"spec_mlp (M=8, I=8192)": time_silu_mul_quant(8, 8192, 200),
+                                 "prefill chunk (M=2048, I=8192)": time_silu_mul_quant(2048, 8192, 50)}
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -1,6 +1,6 @@
 // Quantization kernels for gfx950:
 //   quant_act_kernel       dynamic per-token, group-128 activation quantization
-//   silu_mul_quant_kernel  h = BF16(silu(gate) * up) in FP64, then the same quantization
+//   silu_mul_quant_kernel  h = BF16(silu(gate) * up), rounded once, then the same quantization
 //   quant_weight_kernel    128x128 block weight quantization (offline step)
 //   rmsnorm_quant_kernel   h = BF16(RMSNorm(x) * gamma), rounded once, then the same quantization
 //
@@ -19,6 +19,9 @@
 #include "launch.h"
 
 namespace fp8bs {
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kQuantThreads = 256;           // 16 groups per block pass
 // Groups per 16-lane row: 4 for large inputs (more loads in flight per lane), 1
@@ -88,6 +91,48 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     }
 }
 
+// h = BF16(g u / (1 + e^-g)) for 8 values, exactly rounded.  Float32 first:
+// h32 = fl32(fl32(g u) rcp(fl32(1 + expf(-g)))) has a relative error of at most about
+// 7 float32 ulps (expf and the hardware reciprocal within 1 ulp each, three
+// roundings), so its BF16 rounding (nearest even) is the exact one unless h32 lies
+// within 16 ulps of a BF16 rounding midpoint (low 16 bits in [0x7FF0, 0x8010)), or
+// outside [2^-120, 2^127) in magnitude while g u is not zero (float32 underflow or
+// overflow on the way); those elements (rare) are redone in float64.  g u = 0 gives
+// the signed zero float64 gives.  The tests are collected as wave masks.
+__device__ __forceinline__ void silu_mul8(const float (&gv)[8], const float (&uv)[8], float (&h)[8]) {
+    float h32[8];
+    uint64_t redo_mask = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float gu = gv[i] * uv[i];
+        h32[i] = gu * __builtin_amdgcn_rcpf(1.0f + expf(-gv[i]));
+        const uint32_t b = __float_as_uint(h32[i]);
+        const float a = fabsf(h32[i]);
+        redo_mask |= __builtin_amdgcn_ballot_w64(((b + 16u) & 0xFFE0u) == 0x8000u);
+        redo_mask |= __builtin_amdgcn_ballot_w64(!(a >= 0x1p-120f && a < 0x1p127f)) &
+                     __builtin_amdgcn_ballot_w64(gu != 0.0f);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        const v2f pair = {h32[i], h32[i + 1]};
+        const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, v2bf));
+        h[i] = __uint_as_float(hb << 16);
+        h[i + 1] = __uint_as_float(hb & 0xFFFF0000u);
+    }
+    if (redo_mask) {                                   // wave-uniform; lanes re-test their elements
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t b = __float_as_uint(h32[i]);
+            const float a = fabsf(h32[i]);
+            if (((b + 16u) & 0xFFE0u) == 0x8000u || (!(a >= 0x1p-120f && a < 0x1p127f) && gv[i] * uv[i] != 0.0f)) {
+                const double gd = (double)gv[i];
+                const double silu = gd / (1.0 + exp(-gd));
+                h[i] = bf16_to_f32(f64_to_bf16_rne(silu * (double)uv[i]));
+            }
+        }
+    }
+}
+
 // gu [M, 2I]: gate = columns [0, I), up = [I, 2I).  Group g of h: row g / (I/128),
 // columns 128 (g % (I/128)) + [0, 128).
 template <int kQuantUnroll>
@@ -115,12 +160,7 @@ __global__ __launch_bounds__(kQuantThreads) void silu_mul_quant_kernel(
         float gv[8], uv[8], h[8];
         unpack8(graw[u], gv);
         unpack8(uraw[u], uv);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const double gd = (double)gv[i];
-            const double silu = gd / (1.0 + exp(-gd));
-            h[i] = bf16_to_f32(f64_to_bf16_rne(silu * (double)uv[i]));
-        }
+        silu_mul8(gv, uv, h);
         const float amax = row16_max(absmax8(h));
         const float sc = amax / kE4M3Max;
         reinterpret_cast<uint2*>(q + g * kGroup)[sub] = quant8(h, sc);
@@ -171,8 +211,6 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(
 // U = 0 is the general form for long rows: x and gamma are read again in step 2
 // (from cache).
 constexpr int kNormThreads = 256;
-typedef float v2f __attribute__((ext_vector_type(2)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr int kNormRowsPerPass = kNormThreads / 16;      // groups in flight per pass
 
 // h = BF16((x r) gamma) for 8 values, exactly rounded.  Float32 first:

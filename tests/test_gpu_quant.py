@@ -148,6 +148,55 @@ def test_quant_act_every_x_for_many_scales():
     check_quant(bits, f"every x for {len(amax)} scales")
 
 
+def _silu_probes(rng, count, window):
+    """(g, u) BF16 pairs whose float64 g u / (1 + e^-g) lies within `window` float32
+    ulps of a BF16 rounding midpoint (low 16 bits near 0x8000)."""
+    found = []
+    while sum(len(f[0]) for f in found) < count:
+        g = bf16(rng.standard_normal(1 << 20) * 3.0)
+        u = bf16(rng.standard_normal(1 << 20) * 3.0)
+        gf = oracle.bf16_bits_to_f32(g).astype(np.float64)
+        uf = oracle.bf16_bits_to_f32(u).astype(np.float64)
+        h = gf * uf / (1.0 + np.exp(-gf))
+        low = h.astype(np.float32).view(np.uint32) & 0xFFFF
+        near = np.nonzero((np.abs(low.astype(np.int64) - 0x8000) <= window) & (np.abs(h) > 1e-30))[0]
+        found.append((g[near], u[near]))
+    g = np.concatenate([f[0] for f in found])[:count]
+    u = np.concatenate([f[1] for f in found])[:count]
+    return g, u
+
+
+def test_silu_mul_quant_probes():
+    """Each 128-group holds one probe element that dominates the group, so the group's
+    scale fl32(amax / 448) reads back the probe's BF16 h exactly: probes within 24 float32
+    ulps of a BF16 rounding midpoint (the float64 recomputation), extreme gates (float32
+    exp overflow and underflow) and huge or tiny products, against the oracle."""
+    rng = np.random.default_rng(99)
+    I = 1024
+    groups_per_row = I // 128
+    g_near, u_near = _silu_probes(rng, 2048, 24)
+    extreme_g = np.array([-200, -120, -100, -90, -88, -87, -80, -60, -20, 20, 60, 87, 88, 100, 200], np.float32)
+    extreme_u = np.array([1e36, -1e36, 1e30, 1e-30, -1e-37, 5e-39], np.float32)   # |h| stays below BF16 max
+    eg, eu = np.meshgrid(extreme_g, extreme_u)
+    probes_g = np.concatenate([g_near, bf16(eg.ravel())])
+    probes_u = np.concatenate([u_near, bf16(eu.ravel())])
+    n = len(probes_g)
+    M = (n + groups_per_row - 1) // groups_per_row
+    gate = bf16(rng.standard_normal((M, I)) * 1e-3)       # background: tiny products
+    up = bf16(rng.standard_normal((M, I)) * 1e-3)
+    idx = np.arange(n)
+    rows, cols = idx // groups_per_row, (idx % groups_per_row) * 128 + rng.integers(0, 128, n)
+    gate[rows, cols] = probes_g
+    up[rows, cols] = probes_u
+    gu = np.concatenate([gate, up], axis=1)
+    banner(f"silu_mul_quant probes: {len(g_near)} near midpoints, {eg.size} extreme")
+    q, s = fb.silu_mul_quant(dev_bf16(gu))
+    torch.cuda.synchronize()
+    qo, so = oracle.silu_mul_quant(gu)
+    assert_bits_equal(host_f32(s), so, "probe scales")
+    assert_bits_equal(host_u8(q), qo, "probe codes")
+
+
 def check_rmsnorm(x, g, eps, what):
     banner(f"rmsnorm_quant {what} shape={x.shape}")
     q, s = fb.rmsnorm_quant(dev_bf16(x), dev_bf16(g), eps)
