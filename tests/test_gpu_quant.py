@@ -232,6 +232,28 @@ def test_rmsnorm_quant_redo_path():
     check_rmsnorm(x, g, np.float32(1e-5), f"{near} near-midpoint elements")
 
 
+def test_rmsnorm_quant_probes():
+    """One element per 128-group dominates its group (the rest is a tiny background), so
+    every group scale reads back that element's BF16 h exactly.  16384 rows x 8 probes
+    put a few dozen probes within 8 float32 ulps of a BF16 rounding midpoint, where the
+    kernel recomputes in float64, and many more just outside; the count is taken on the
+    host first."""
+    rng = np.random.default_rng(77)
+    M, K = 16384, 1024
+    x = bf16(rng.standard_normal((M, K)) * 1e-4)
+    cols = np.arange(0, K, 128)[None, :] + rng.integers(0, 128, (M, K // 128))
+    rows = np.repeat(np.arange(M)[:, None], K // 128, axis=1)
+    x[rows, cols] = bf16(rng.standard_normal((M, K // 128)) * 4.0)
+    g = bf16(rng.standard_normal(K) * 0.3 + 1.0)
+    xf = oracle.bf16_bits_to_f32(x).astype(np.float64)
+    r = 1.0 / np.sqrt(np.mean(xf * xf, axis=1, keepdims=True) + 1e-5)
+    h = (xf * r * oracle.bf16_bits_to_f32(g).astype(np.float64))[rows, cols]
+    low = h.astype(np.float32).view(np.uint32).astype(np.int64) & 0xFFFF
+    near = int(np.count_nonzero(np.abs(low - 0x8000) <= 8))
+    assert near > 20, near
+    check_rmsnorm(x, g, np.float32(1e-5), f"probes ({near} within 8 ulps of a midpoint)")
+
+
 def test_rmsnorm_quant_edge_rows():
     rng = np.random.default_rng(3)
     K = 1024
