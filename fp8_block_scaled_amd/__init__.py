@@ -117,19 +117,22 @@ def workspace_size(M, N, K):
 
 
 def get_workspace(device, nbytes):
-    """A workspace of at least ``nbytes`` for ``device``, cached per device.
+    """A workspace of at least ``nbytes`` for ``device`` and its current stream, cached
+    per (device, stream).
 
-    No call reads workspace it has not written earlier in the same call, so the
-    buffer is reused as is.  Calls on one device through this cache share it: they
-    must be ordered (one stream), as the library requires for a shared workspace.
+    No call reads workspace it has not written earlier in the same call, so the buffer
+    is neither cleared nor initialized (no fill is enqueued, also under graph capture).
+    Calls on one stream run in order, so they can share it; calls on different streams
+    get different buffers, each allocated while its stream is current.
     """
     device = torch.device(device)
-    key = device.index if device.index is not None else torch.cuda.current_device()
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    key = (index, torch.cuda.current_stream(index).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         size = max(nbytes, 1 << 20)
         size = (size + 255) // 256 * 256
-        ws = torch.zeros(size, dtype=torch.uint8, device=device)
+        ws = torch.empty(size, dtype=torch.uint8, device=torch.device("cuda", index))
         _workspaces[key] = ws
     return ws
 

@@ -253,6 +253,35 @@ def test_split_k(M, N, K, split, monkeypatch):
     assert np.array_equal(gpu_path(x, w, workspace=ws), y)
 
 
+def test_default_workspace_per_stream():
+    """The binding's default workspace is one buffer per (device, stream): split-K calls
+    on two streams at once give the same bits as the same calls in sequence."""
+    M, N, K = 128, 2048, 4096
+    cases = [inputs(M, N, K, seed=40 + i) for i in range(2)]
+    dev_in = []
+    for x, w in cases:
+        q, s = fb.quant_act(dev_bf16(x))
+        qw, ws = fb.quant_weight(dev_bf16(w))
+        dev_in.append((q, s, qw, ws))
+    assert fb.workspace_size(M, N, K) > 0
+    want = [host_u16(fb.block_linear(*a)) for a in dev_in]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(5):
+        for st, a in zip(streams, dev_in):
+            with torch.cuda.stream(st):
+                outs.append(fb.block_linear(*a))
+    torch.cuda.synchronize()
+    for i, y in enumerate(outs):
+        assert np.array_equal(host_u16(y), want[i % 2]), i
+    with torch.cuda.stream(streams[0]):
+        w0 = fb.get_workspace("cuda", 1)
+    with torch.cuda.stream(streams[1]):
+        w1 = fb.get_workspace("cuda", 1)
+    assert w0.data_ptr() != w1.data_ptr()
+
+
 def test_split_k_workspace_sizes():
     """A smaller workspace selects a smaller split or none; every result is in tolerance."""
     M, N, K = 128, 2048, 4096
