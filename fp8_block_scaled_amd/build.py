@@ -69,5 +69,24 @@ def build(verbose=False, jobs=None):
     return LIB
 
 
+C_ABI_SRC = os.path.join(ROOT, "tests", "c_abi", "abi_roundtrip.c")
+C_ABI_BIN = os.path.join(ROOT, "tests", "c_abi", "abi_roundtrip")
+
+
+def build_c_abi_check(verbose=False):
+    """Compile the plain-C caller of the ABI (host code only, gcc) against libfp8bs.so;
+    a GPU test runs it.  Needs the library built first."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler for the ABI check")
+    _run([cc, "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{os.path.join(ROOT, 'include')}",
+          f"-I{os.path.join(rocm, 'include')}", C_ABI_SRC, f"-L{PKG}", "-lfp8bs", f"-L{os.path.join(rocm, 'lib')}",
+          "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN/../../fp8_block_scaled_amd",
+          f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-o", C_ABI_BIN], verbose)
+    return C_ABI_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_c_abi_check(verbose="-v" in sys.argv))
