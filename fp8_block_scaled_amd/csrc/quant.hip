@@ -210,8 +210,12 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(
 //      amax, scale and codes as in quant_act_kernel.
 // U = 0 is the general form for long rows: x and gamma are read again in step 2
 // (from cache).
+// Threads per row: 256, or 1024 for a few rows (a decode batch), where one
+// workgroup per row leaves most CUs idle and the row's latency is the call's time:
+// four times the threads cut the serial chain of groups per thread by four.
 constexpr int kNormThreads = 256;
-constexpr int kNormRowsPerPass = kNormThreads / 16;      // groups in flight per pass
+constexpr int kNormThreadsFew = 1024;
+constexpr int64_t kNormFewRows = 64;
 
 // h = BF16((x r) gamma) for 8 values, exactly rounded.  Float32 first:
 // h32 = fl32(fl32(x r32) gamma) is within 4 float32 ulps of the exact product, so its
@@ -265,11 +269,11 @@ __device__ __forceinline__ double rsqrt_f64(double a) {
     return y;
 }
 
-template <int U>
-__global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
+template <int U, int NT>
+__global__ __launch_bounds__(NT) void rmsnorm_quant_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, double eps, double inv_k, uint8_t* __restrict__ q,
     float* __restrict__ s, int64_t K) {
-    __shared__ double part[kNormThreads / 64];
+    __shared__ double part[NT / 64];
     const int64_t m = blockIdx.x;
     const uint16_t* xr = x + m * K;
     const int grow = threadIdx.x >> 4;
@@ -282,7 +286,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
         // x and gamma chunks requested together, before the reduction
 #pragma unroll
         for (int u = 0; u < UR; ++u) {
-            const int64_t j = grow + kNormRowsPerPass * u;
+            const int64_t j = grow + (NT / 16) * u;
             if (j < groups) {
                 xraw[u] = reinterpret_cast<const uint4*>(xr + j * kGroup)[sub];
                 graw[u] = reinterpret_cast<const uint4*>(gamma + j * kGroup)[sub];
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
         }
 #pragma unroll
         for (int u = 0; u < UR; ++u) {
-            const int64_t j = grow + kNormRowsPerPass * u;
+            const int64_t j = grow + (NT / 16) * u;
             if (j >= groups) continue;
             float v[8];
             unpack8(xraw[u], v);
@@ -298,7 +302,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
             for (int i = 0; i < 8; ++i) ss += (double)v[i] * (double)v[i];
         }
     } else {
-        for (int64_t j = grow; j < groups; j += kNormRowsPerPass) {
+        for (int64_t j = grow; j < groups; j += (NT / 16)) {
             float v[8];
             unpack8(reinterpret_cast<const uint4*>(xr + j * kGroup)[sub], v);
 #pragma unroll
@@ -311,7 +315,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
     __syncthreads();
     double total = 0.0;
 #pragma unroll
-    for (int w = 0; w < kNormThreads / 64; ++w) total += part[w];
+    for (int w = 0; w < NT / 64; ++w) total += part[w];
     const double r = rsqrt_f64(total * inv_k + eps);
     const float r32 = (float)r;
 
@@ -328,37 +332,53 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
     if (U > 0) {
 #pragma unroll
         for (int u = 0; u < UR; ++u) {
-            const int64_t j = grow + kNormRowsPerPass * u;
+            const int64_t j = grow + (NT / 16) * u;
             if (j < groups) emit(j, xraw[u], graw[u]);
         }
     } else {
-        for (int64_t j = grow; j < groups; j += kNormRowsPerPass)
+        for (int64_t j = grow; j < groups; j += (NT / 16))
             emit(j, reinterpret_cast<const uint4*>(xr + j * kGroup)[sub],
                  reinterpret_cast<const uint4*>(gamma + j * kGroup)[sub]);
+    }
+}
+
+template <int NT>
+static void launch_norm(int64_t M, int64_t K, const uint16_t* xp, const uint16_t* gp, double e, double inv_k, void* q,
+                        float* s, hipStream_t st) {
+    const int64_t passes = (K / kGroup + NT / 16 - 1) / (NT / 16);     // groups in flight per pass: NT / 16
+    const dim3 grid((unsigned)M), block(NT);
+    if (passes <= 1)
+        hipLaunchKernelGGL((rmsnorm_quant_kernel<1, NT>), grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
+    else if (passes <= 2)
+        hipLaunchKernelGGL((rmsnorm_quant_kernel<2, NT>), grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
+    else if (passes <= 4)
+        hipLaunchKernelGGL((rmsnorm_quant_kernel<4, NT>), grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
+    else if (passes <= 8)
+        hipLaunchKernelGGL((rmsnorm_quant_kernel<8, NT>), grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
+    else {
+        // 16 chunks per thread fit the registers of 256-thread workgroups only.
+        if constexpr (NT <= kNormThreads) {
+            if (passes <= 16) {
+                hipLaunchKernelGGL((rmsnorm_quant_kernel<16, NT>), grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q,
+                                   s, K);
+                return;
+            }
+        }
+        hipLaunchKernelGGL((rmsnorm_quant_kernel<0, NT>), grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
     }
 }
 
 hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, float eps, void* q, float* s, int64_t M, int64_t K,
                                 hipStream_t st) {
     if (M == 0) return hipSuccess;
-    const int64_t passes = (K / kGroup + kNormRowsPerPass - 1) / kNormRowsPerPass;
-    const dim3 grid((unsigned)M), block(kNormThreads);
     const uint16_t* xp = (const uint16_t*)x;
     const uint16_t* gp = (const uint16_t*)gamma;
     const double e = (double)eps;
     const double inv_k = 1.0 / (double)K;
-    if (passes <= 1)
-        hipLaunchKernelGGL(rmsnorm_quant_kernel<1>, grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
-    else if (passes <= 2)
-        hipLaunchKernelGGL(rmsnorm_quant_kernel<2>, grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
-    else if (passes <= 4)
-        hipLaunchKernelGGL(rmsnorm_quant_kernel<4>, grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
-    else if (passes <= 8)
-        hipLaunchKernelGGL(rmsnorm_quant_kernel<8>, grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
-    else if (passes <= 16)
-        hipLaunchKernelGGL(rmsnorm_quant_kernel<16>, grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
+    if (M <= kNormFewRows)
+        launch_norm<kNormThreadsFew>(M, K, xp, gp, e, inv_k, q, s, st);
     else
-        hipLaunchKernelGGL(rmsnorm_quant_kernel<0>, grid, block, 0, st, xp, gp, e, inv_k, (uint8_t*)q, s, K);
+        launch_norm<kNormThreads>(M, K, xp, gp, e, inv_k, q, s, st);
     return hipGetLastError();
 }
 
