@@ -207,8 +207,10 @@ def check_rmsnorm(x, g, eps, what):
 
 
 @pytest.mark.parametrize("M,K", [(1, 128), (1, 7168), (5, 384), (37, 2048), (300, 1024), (8, 21504), (2000, 1024),
-                                 (3, 4096), (2, 8192), (2, 33024)])
+                                 (3, 4096), (2, 8192), (2, 33024), (64, 1152), (65, 1152), (1, 66048)])
 def test_rmsnorm_quant_random(M, K):
+    # (64, 1152) and (65, 1152) sit on both sides of the switch to 1024-thread workgroups
+    # for few rows; (1, 66048) takes the few-rows kernel's re-reading form (over 8 passes).
     rng = np.random.default_rng(M * 7 + K)
     x = bf16(rng.standard_normal((M, K)) * 10.0 ** rng.integers(-3, 4, (M, 1)))
     g = bf16(rng.standard_normal(K) * 0.3 + 1.0)
