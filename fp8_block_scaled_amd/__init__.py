@@ -47,28 +47,63 @@ def _call(fn_name, device, *args):
 
 
 def _check_tensor(t, name, dtypes, ndim):
-    if not isinstance(t, torch.Tensor):
-        raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a GPU device (there is no CPU path)")
-    if t.dtype not in dtypes:
-        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
-    if t.dim() != ndim:
-        raise ValueError(f"{name} must be {ndim}-D")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    """Type, dtype, number of dimensions and contiguity of one tensor (devices are
+    checked by _check_tensors once every operand's shape is known)."""
+    _check_tensors([(t, name, dtypes, ndim)], devices=False)
+
+
+def _check_tensors(specs, devices=True):
+    """Validate tensors before any pointer reaches the library.
+
+    ``specs``: (tensor, name, dtypes, shape) with shape an int (the number of
+    dimensions) or a tuple (the exact shape).  Every tensor is checked for type,
+    dtype, shape and contiguity first, then all of them for being on one GPU: a
+    wrong-sized output would otherwise let a kernel write past its allocation,
+    which the C layer cannot detect.
+    """
+    for t, name, dtypes, shape in specs:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype not in dtypes:
+            raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+        if isinstance(shape, int):
+            if t.dim() != shape:
+                raise ValueError(f"{name} must be {shape}-D, got shape {tuple(t.shape)}")
+        elif tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not devices:
+        return
+    dev = None
+    for t, name, _, _ in specs:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device (there is no CPU path)")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other operands on {dev}: all must be on one GPU")
 
 
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16) if hasattr(torch, "uint16") else (torch.bfloat16, torch.int16)
 _CODES = (torch.uint8, torch.float8_e4m3fn)
 
 
+def _quant_outputs(x, q, s, M, K):
+    """Allocate (or check) the codes [M, K] and scales [M, K/128] of a quantizer."""
+    if K % 128:
+        raise ValueError(f"K = {K} must be a multiple of 128")
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
+    s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if s is None else s
+    _check_tensors([(x, "input", _BF16, 2), (q, "q", _CODES, (M, K)), (s, "s", (torch.float32,), (M, K // 128))])
+    return q, s
+
+
 def quant_act(x, q=None, s=None):
     """Per-token group-128 quantization of BF16 x [M, K] -> (q uint8 [M, K], s f32 [M, K/128])."""
     _check_tensor(x, "x", _BF16, 2)
     M, K = x.shape
-    q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
-    s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if s is None else s
+    q, s = _quant_outputs(x, q, s, M, K)
     _call("fp8_quant_act", x.device, x.data_ptr(), q.data_ptr(), s.data_ptr(), M, K)
     return q, s
 
@@ -77,8 +112,11 @@ def quant_weight(w):
     """128x128 block quantization of BF16 w [N, K] -> (qw uint8 [N, K], ws f32 [N/128, K/128])."""
     _check_tensor(w, "w", _BF16, 2)
     N, K = w.shape
+    if N % 128 or K % 128:
+        raise ValueError(f"N = {N} and K = {K} must be multiples of 128")
     qw = torch.empty((N, K), dtype=torch.uint8, device=w.device)
     ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+    _check_tensors([(w, "w", _BF16, 2), (qw, "qw", _CODES, (N, K)), (ws, "ws", (torch.float32,), (N // 128, K // 128))])
     _call("fp8_quant_weight", w.device, w.data_ptr(), qw.data_ptr(), ws.data_ptr(), N, K)
     return qw, ws
 
@@ -90,8 +128,7 @@ def silu_mul_quant(gu, q=None, s=None):
     if two_i % 2:
         raise ValueError("gate/up width must be even")
     I = two_i // 2
-    q = torch.empty((M, I), dtype=torch.uint8, device=gu.device) if q is None else q
-    s = torch.empty((M, I // 128), dtype=torch.float32, device=gu.device) if s is None else s
+    q, s = _quant_outputs(gu, q, s, M, I)
     _call("fp8_silu_mul_quant", gu.device, gu.data_ptr(), q.data_ptr(), s.data_ptr(), M, I)
     return q, s
 
@@ -100,14 +137,12 @@ def rmsnorm_quant(x, gamma, eps, q=None, s=None):
     """Codes and scales of BF16(x / sqrt(mean(x^2) + eps) * gamma) for BF16 x [M, K]
     and gamma [K] (FP64 evaluation, one BF16 rounding), quantized per token and group."""
     _check_tensor(x, "x", _BF16, 2)
-    _check_tensor(gamma, "gamma", _BF16, 1)
     M, K = x.shape
+    _check_tensor(gamma, "gamma", _BF16, 1)
     if gamma.shape[0] != K:
-        raise ValueError("gamma must have K elements")
-    if gamma.device != x.device:
-        raise ValueError("x and gamma must be on the same device")
-    q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
-    s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if s is None else s
+        raise ValueError(f"gamma must have shape ({K},), got shape {tuple(gamma.shape)}")
+    q, s = _quant_outputs(x, q, s, M, K)
+    _check_tensors([(x, "x", _BF16, 2), (gamma, "gamma", _BF16, (K,))])
     _call("fp8_rmsnorm_quant", x.device, x.data_ptr(), gamma.data_ptr(), float(eps), q.data_ptr(), s.data_ptr(), M, K)
     return q, s
 
@@ -140,17 +175,20 @@ def get_workspace(device, nbytes):
 def block_linear(q, s, qw, ws, out=None, workspace=None):
     """y [M, N] bf16 = (q * s) @ (qw * ws)^T with FP32 accumulation per 128-wide K block."""
     _check_tensor(q, "q", _CODES, 2)
-    _check_tensor(s, "s", (torch.float32,), 2)
     _check_tensor(qw, "qw", _CODES, 2)
-    _check_tensor(ws, "ws", (torch.float32,), 2)
     M, K = q.shape
     N = qw.shape[0]
     if qw.shape[1] != K:
         raise ValueError("q and qw disagree on K")
-    if s.shape != (M, K // 128) or ws.shape != (N // 128, K // 128):
-        raise ValueError("scale shapes do not match the operands")
+    if K % 128 or N % 128:
+        raise ValueError(f"K = {K} and N = {N} must be multiples of 128")
     dev = q.device
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    specs = [(q, "q", _CODES, (M, K)), (s, "s", (torch.float32,), (M, K // 128)), (qw, "qw", _CODES, (N, K)),
+             (ws, "ws", (torch.float32,), (N // 128, K // 128)), (y, "out", _BF16, (M, N))]
+    if workspace is not None:
+        specs.append((workspace, "workspace", (torch.uint8,), 1))
+    _check_tensors(specs)
     if workspace is None:
         need = workspace_size(M, N, K) if K > 0 else 0
         workspace = get_workspace(dev, need) if need else None
@@ -176,13 +214,17 @@ def nvfp4_linear(x, w4, bs, g, out=None, workspace=None):
     """
     _check_tensor(x, "x", _BF16, 2)
     _check_tensor(w4, "w4", (torch.uint8,), 2)
-    _check_tensor(bs, "bs", _CODES, 2)
     M, K = x.shape
     N = w4.shape[0]
-    if w4.shape[1] * 2 != K or bs.shape != (N, K // 16):
-        raise ValueError("w4 must be [N, K/2] and bs [N, K/16]")
+    if w4.shape[1] * 2 != K:
+        raise ValueError("w4 must be [N, K/2]")
     dev = x.device
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    specs = [(x, "x", _BF16, (M, K)), (w4, "w4", (torch.uint8,), (N, K // 2)), (bs, "bs", _CODES, (N, K // 16)),
+             (y, "out", _BF16, (M, N))]
+    if workspace is not None:
+        specs.append((workspace, "workspace", (torch.uint8,), 1))
+    _check_tensors(specs)
     if workspace is None:
         need = nvfp4_workspace_size(M, N, K) if K > 0 and K % 128 == 0 and N % 128 == 0 else 0
         workspace = get_workspace(dev, need) if need else None

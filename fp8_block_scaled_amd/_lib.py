@@ -8,7 +8,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libfp8bs.so")
+# FP8BS_LIBRARY names another build of the same library (the host-sanitized build
+# that the ABI validation tests load); by default the in-tree libfp8bs.so.
+LIB_PATH = os.environ.get("FP8BS_LIBRARY") or os.path.join(_PKG, "libfp8bs.so")
 
 # Header constants (include/fp8bs.h).
 FP8BS_OK = 0

@@ -69,6 +69,41 @@ def build(verbose=False, jobs=None):
     return LIB
 
 
+SAN_LIB = os.path.join(BUILD, "libfp8bs_hostsan.so")
+
+
+def sanitizer_runtime():
+    """The clang AddressSanitizer runtime (it carries UBSan too) that a process loading
+    the host-sanitized library must preload."""
+    rocm_llvm = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(HIPCC))), "llvm")
+    clang_dir = os.path.join(rocm_llvm, "lib", "clang")
+    for ver in sorted(os.listdir(clang_dir), reverse=True) if os.path.isdir(clang_dir) else []:
+        p = os.path.join(clang_dir, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return p
+    raise RuntimeError("clang AddressSanitizer runtime not found")
+
+
+def build_sanitized_abi(verbose=False):
+    """Build a second copy of the library whose host code in api.hip (argument
+    validation, device check, schedule choice) is instrumented with AddressSanitizer
+    and UndefinedBehaviorSanitizer; device code and the other sources are the normal
+    objects.  tests/test_abi_sanitized.py runs the ABI validation tests against it on
+    the CPU.  Needs build() first (it links build()'s objects)."""
+    os.makedirs(BUILD, exist_ok=True)
+    obj = os.path.join(BUILD, "api_hostsan.o")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    flags = [f for f in CFLAGS if f != "-O3"] + ["-O1", "-g"]
+    _run([HIPCC, *flags, *san, "-c", os.path.join(CSRC, "api.hip"), "-o", obj], verbose)
+    objs = [os.path.join(BUILD, src.replace(".hip", ".o")) for src in SOURCES if src != "api.hip"]
+    tmp = SAN_LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, *objs, "-shared-libsan",
+          "-fsanitize=address,undefined", "-o", tmp], verbose)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 C_ABI_SRC = os.path.join(ROOT, "tests", "c_abi", "abi_roundtrip.c")
 C_ABI_BIN = os.path.join(ROOT, "tests", "c_abi", "abi_roundtrip")
 
@@ -90,3 +125,4 @@ def build_c_abi_check(verbose=False):
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
     print(build_c_abi_check(verbose="-v" in sys.argv))
+    print(build_sanitized_abi(verbose="-v" in sys.argv))

@@ -49,6 +49,11 @@ typedef enum {
 
 /*
  * Dynamic per-token, group-128 activation quantization.
+ * Defined by the "Nanbeige4.3-33B FP8" model card: its introduction gives E4M3 codes
+ * with dynamic activation scales per token and group of 128, and its section
+ * "Recipe and calibration" calls the scales standard minmax (data independent).
+ * The scale type (FP32), the scale formula amax / 448, the float32 quotient, the
+ * rounding and the zero-group rule below are this library's readings of that text.
  *   x_bf16 [M, K]      BF16 input (in).
  *   q_e4m3 [M, K]      E4M3 codes (out).
  *   s_f32  [M, K/128]  scales (out); s[m, g] covers x[m, 128 g .. 128 g + 127].
@@ -56,12 +61,18 @@ typedef enum {
  * (IEEE float32 division, round to nearest even, subnormals kept);
  * q = E4M3(fl32(x / s)) rounded to nearest even and saturated at +-448.  A group
  * whose amax is 0 gets s = +0.0 and codes 0x00.  Bit-exact and deterministic.
+ * Ownership: x is read only; q and s are written completely (every element).
+ * Errors: FP8BS_ERR_SHAPE (K not a multiple of 128, M < 0, overflow),
+ * FP8BS_ERR_NULL, FP8BS_ERR_ALIGN, FP8BS_ERR_DEVICE, FP8BS_ERR_HIP; on an error
+ * nothing is enqueued.
  */
 int fp8_quant_act(const void* x_bf16, void* q_e4m3, float* s_f32,
                   int64_t M, int64_t K, hipStream_t stream);
 
 /*
  * 128x128 block weight quantization (offline step; same rounding as above).
+ * "Nanbeige4.3-33B FP8" card, "Recipe and calibration": one scale per 128x128 weight
+ * block from standard minmax quantization, which needs no calibration data.
  *   w_bf16  [N, K]            BF16 weights, row n = output channel n (in).
  *   qw_e4m3 [N, K]            E4M3 codes (out).
  *   ws_f32  [N/128, K/128]    scales (out); ws[i, j] covers rows 128 i .. 128 i + 127
@@ -73,7 +84,8 @@ int fp8_quant_weight(const void* w_bf16, void* qw_e4m3, float* ws_f32,
 
 /*
  * Input of the down projection: h = BF16(silu(gate) * up), then the activation
- * quantization above applied to h.
+ * quantization above applied to h ("Nanbeige4.3-33B DFlash2" card, "Architecture and
+ * checkpoint format": separate gate and up tensors, MLP width 8192).
  *   gu_bf16 [M, 2 I]    fused gate/up output: gate = columns [0, I), up = [I, 2 I).
  *   q_e4m3  [M, I]      E4M3 codes of h (out).
  *   s_f32   [M, I/128]  scales of h (out).
@@ -103,6 +115,12 @@ int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, float eps,
 
 /*
  * Block-scaled FP8 GEMM: y = (q * s) @ (w * ws)^T, accumulated in FP32, stored BF16.
+ * Defined by the "Nanbeige4.3-33B FP8" model card: introduction and "Recipe and
+ * calibration" (E4M3 weights with one scale per 128x128 block, activations with
+ * dynamic per-token group-128 scales), "Serving" (the model runs with --dtype
+ * bfloat16, hence a BF16 output) and "Compatibility and limitations" (results are
+ * not promised bit-identical across kernel geometries, hence a tolerance rather than
+ * one summation order).
  *   q_e4m3  [M, K]            activation codes; s_f32 [M, K/128] their scales.
  *   w_e4m3  [N, K]            weight codes;     ws_f32 [N/128, K/128] block scales.
  *   y_bf16  [M, N]            output (out), rounded to BF16 (nearest even) once.
@@ -119,6 +137,10 @@ int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, float eps,
  * for a given (M, N, K, device, workspace size), so repeated calls give
  * bitwise-identical outputs.  Accuracy: |y - ref| <= 4e-3 |ref| + 1e-3 rms(ref)
  * against the exact dequantize-and-matmul.
+ * Ownership: q, s, w, ws are read only; y is written completely; the workspace
+ * is scratch the call may overwrite.  Errors: FP8BS_ERR_SHAPE (K <= 0, K or N not a
+ * multiple of 128, overflow), FP8BS_ERR_NULL, FP8BS_ERR_ALIGN, FP8BS_ERR_WORKSPACE,
+ * FP8BS_ERR_DEVICE, FP8BS_ERR_HIP; on an error nothing is enqueued.
  */
 int fp8_block_linear(const void* q_e4m3, const float* s_f32,
                      const void* w_e4m3, const float* ws_f32,

@@ -159,3 +159,53 @@ def test_nvfp4_binding_rejects_bad_tensors_before_any_gpu_call():
         fb.nvfp4_linear(x, w4, bs, 1.0)
     with pytest.raises(TypeError):                        # not a tensor
         fb.nvfp4_linear([[0.0] * 256] * 2, w4, bs, 1.0)
+
+
+def test_binding_rejects_wrong_outputs_before_any_gpu_call():
+    """Caller-supplied outputs (q, s, out) and operands are checked for dtype, exact
+    shape and contiguity before any pointer reaches the library: a wrong-sized output
+    would let a kernel write past its allocation."""
+    import torch
+    import fp8_block_scaled_amd as fb
+    bf = torch.bfloat16
+    x = torch.zeros((4, 256), dtype=bf)
+    q_ok = torch.zeros((4, 256), dtype=torch.uint8)
+    s_ok = torch.zeros((4, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="shape"):
+        fb.quant_act(x, q=torch.zeros((4, 128), dtype=torch.uint8), s=s_ok)
+    with pytest.raises(ValueError, match="shape"):
+        fb.quant_act(x, q=q_ok, s=torch.zeros((4, 1), dtype=torch.float32))
+    with pytest.raises(TypeError):
+        fb.quant_act(x, q=q_ok, s=torch.zeros((4, 2), dtype=torch.float64))
+    with pytest.raises(ValueError, match="contiguous"):
+        fb.quant_act(x, q=torch.zeros((256, 4), dtype=torch.uint8).t(), s=s_ok)
+    with pytest.raises(ValueError, match="multiple of 128"):
+        fb.quant_act(torch.zeros((4, 200), dtype=bf))
+    gu = torch.zeros((4, 512), dtype=bf)
+    with pytest.raises(ValueError, match="shape"):
+        fb.silu_mul_quant(gu, q=torch.zeros((4, 512), dtype=torch.uint8), s=s_ok)
+    with pytest.raises(ValueError, match="shape"):
+        fb.rmsnorm_quant(x, torch.zeros((128,), dtype=bf), 1e-5)
+    with pytest.raises(ValueError, match="shape"):
+        fb.rmsnorm_quant(x, torch.zeros((256,), dtype=bf), 1e-5, q=q_ok, s=torch.zeros((2, 4), dtype=torch.float32))
+    qw = torch.zeros((128, 256), dtype=torch.uint8)
+    ws = torch.zeros((1, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="shape"):
+        fb.block_linear(q_ok, s_ok, qw, ws, out=torch.zeros((4, 256), dtype=bf))
+    with pytest.raises(ValueError, match="shape"):
+        fb.block_linear(q_ok, torch.zeros((2, 4), dtype=torch.float32), qw, ws)
+    with pytest.raises(ValueError, match="shape"):
+        fb.block_linear(q_ok, s_ok, qw, torch.zeros((2, 1), dtype=torch.float32))
+    with pytest.raises(TypeError):
+        fb.block_linear(q_ok, s_ok, qw, ws, out=torch.zeros((4, 128), dtype=torch.float32))
+    with pytest.raises(TypeError):
+        fb.block_linear(q_ok, s_ok, qw, ws, workspace=torch.zeros(1024, dtype=torch.float32))
+    w4 = torch.zeros((128, 128), dtype=torch.uint8)
+    bs = torch.zeros((128, 16), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="shape"):
+        fb.nvfp4_linear(x, w4, bs, 1.0, out=torch.zeros((4, 256), dtype=bf))
+    with pytest.raises(ValueError, match="shape"):
+        fb.nvfp4_linear(x, w4, torch.zeros((128, 8), dtype=torch.uint8), 1.0)
+    # Correct shapes on the CPU: rejected for the device, not for a shape.
+    with pytest.raises(ValueError, match="GPU"):
+        fb.block_linear(q_ok, s_ok, qw, ws, out=torch.zeros((4, 128), dtype=bf))

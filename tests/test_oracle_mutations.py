@@ -14,6 +14,7 @@ from tests import test_oracle_e4m3 as te
 from tests import test_oracle_linear as tl
 from tests import test_oracle_nvfp4 as tn
 from tests import test_oracle_quant as tq
+from tests import test_oracle_quotient as tqq
 from tests import test_oracle_rmsnorm as tr
 from tests import test_oracle_silu as ts
 
@@ -49,6 +50,47 @@ def _quant_groups_reciprocal(x, axes):
     q = e4m3.encode_rne_sat(np.clip(v, -448, 448))
     q = np.where(np.broadcast_to(zero, q.shape), np.uint8(0), q).astype(np.uint8)
     return q, np.squeeze(s, axis=axes).astype(np.float32)
+
+
+def _quant_groups_quotient(kind):
+    """_quant_groups with the quotient formed as x * fl32(1 / s) ("reciprocal") or as
+    x * fl32(448 / amax) ("inverse_scale"), guarded the way a kernel would guard it:
+    groups with s < 2^-60 keep the division."""
+    def f(x, axes):
+        amax = np.max(np.abs(x), axis=axes, keepdims=True)
+        s = (amax / np.float32(448)).astype(np.float32)
+        zero = s == 0
+        safe = np.where(zero, np.float32(1), s)
+        with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+            if kind == "reciprocal":
+                y = (np.float32(1) / safe).astype(np.float32)
+            else:
+                y = (np.float32(448) / np.where(zero, np.float32(1), amax)).astype(np.float32)
+            fast = (x * y).astype(np.float32)
+            exact = (x / safe).astype(np.float32)
+        v = np.where(s >= np.float32(2.0 ** -60), fast, exact)
+        q = e4m3.encode_rne_sat(np.clip(v, -448, 448))
+        q = np.where(np.broadcast_to(zero, q.shape), np.uint8(0), q).astype(np.uint8)
+        return q, np.squeeze(s, axis=axes).astype(np.float32)
+    return f
+
+
+def _quant_act_with(groups_fn):
+    def f(x_bits):
+        x_bits = np.asarray(x_bits, dtype=np.uint16)
+        M, K = x_bits.shape
+        q, s = groups_fn(quant.bf16_bits_to_f32(x_bits).reshape(M, K // 128, 128), (2,))
+        return q.reshape(M, K), s.reshape(M, K // 128)
+    return f
+
+
+def _quant_weight_with(groups_fn):
+    def f(w_bits):
+        w_bits = np.asarray(w_bits, dtype=np.uint16)
+        N, K = w_bits.shape
+        q, s = groups_fn(quant.bf16_bits_to_f32(w_bits).reshape(N // 128, 128, K // 128, 128), (1, 3))
+        return q.reshape(N, K), s.reshape(N // 128, K // 128)
+    return f
 
 
 def _quant_act_strided_groups(x_bits):
@@ -149,6 +191,22 @@ MUTATIONS = {
                      [tq.test_negation_flips_sign_bits_only]),
     "scale_by_reciprocal": ([(quant, "_quant_groups", _quant_groups_reciprocal)],
                             [tq.test_scale_is_correctly_rounded_amax_over_448]),
+    "act_quotient_by_reciprocal": (
+        [(quant, "quant_act", _quant_act_with(_quant_groups_quotient("reciprocal"))),
+         (oracle, "quant_act", _quant_act_with(_quant_groups_quotient("reciprocal")))],
+        [tqq.test_activation_codes_every_bf16_x_for_2040_amax_values]),
+    "act_quotient_by_448_over_amax": (
+        [(quant, "quant_act", _quant_act_with(_quant_groups_quotient("inverse_scale"))),
+         (oracle, "quant_act", _quant_act_with(_quant_groups_quotient("inverse_scale")))],
+        [tqq.test_activation_codes_every_bf16_x_for_2040_amax_values]),
+    "weight_quotient_by_reciprocal": (
+        [(quant, "quant_weight", _quant_weight_with(_quant_groups_quotient("reciprocal"))),
+         (oracle, "quant_weight", _quant_weight_with(_quant_groups_quotient("reciprocal")))],
+        [tqq.test_weight_codes_every_bf16_x_for_765_amax_values]),
+    "weight_quotient_by_448_over_amax": (
+        [(quant, "quant_weight", _quant_weight_with(_quant_groups_quotient("inverse_scale"))),
+         (oracle, "quant_weight", _quant_weight_with(_quant_groups_quotient("inverse_scale")))],
+        [tqq.test_weight_codes_every_bf16_x_for_765_amax_values]),
     "strided_groups": ([(quant, "quant_act", _quant_act_strided_groups), (oracle, "quant_act", _quant_act_strided_groups)],
                        [tq.test_group_structure_spike]),
     "weight_grid_transposed": ([(linear, "dequant_weight", _dequant_weight_transposed)],
