@@ -110,6 +110,26 @@ def test_silu_mul_quant(M, I, sigma):
     assert_bits_equal(host_u8(q), qo, "silu codes")
 
 
+@pytest.mark.parametrize("M,I", [(1023, 8192), (1024, 8192), (2048, 8192)])
+def test_silu_mul_quant_both_sides_of_the_unrolled_form(M, I):
+    """1023 x 8192 (65,472 groups) runs the one-group-per-row form, 1024 x 8192 (exactly
+    65,536 groups) and 2048 x 8192 (the chunked-prefill size the bench times) the
+    unrolled one; near-midpoint probes are planted in every row, 8 per row."""
+    rng = np.random.default_rng(M + I)
+    gu = bf16(rng.standard_normal((M, 2 * I)) * 1.7)
+    g_near, u_near = _silu_probes(rng, 8 * M, 24)
+    rows = np.repeat(np.arange(M), 8)
+    cols = rng.integers(0, I, 8 * M)
+    gu[rows, cols] = g_near
+    gu[rows, I + cols] = u_near
+    banner(f"silu_mul_quant M={M} I={I} ({M * I // 128} groups)")
+    q, s = fb.silu_mul_quant(dev_bf16(gu))
+    torch.cuda.synchronize()
+    qo, so = oracle.silu_mul_quant(gu)
+    assert_bits_equal(host_f32(s), so, "silu scales")
+    assert_bits_equal(host_u8(q), qo, "silu codes")
+
+
 def test_quant_is_deterministic():
     rng = np.random.default_rng(99)
     x = dev_bf16(bf16(rng.standard_normal((257, 2048))))
@@ -215,6 +235,40 @@ def test_rmsnorm_quant_random(M, K):
     x = bf16(rng.standard_normal((M, K)) * 10.0 ** rng.integers(-3, 4, (M, 1)))
     g = bf16(rng.standard_normal(K) * 0.3 + 1.0)
     check_rmsnorm(x, g, np.float32(1e-5), "random")
+
+
+# Each shape reaches one form of the kernel (chunks per thread U, threads per row NT):
+# 256 threads above 64 rows, 1024 up to 64 rows; U = groups per thread rounded up to
+# 1, 2, 4, 8, 16 (256 threads only), else 0 (the form that re-reads x and gamma).
+@pytest.mark.parametrize("M,K,form", [(70, 2048, "<1,256>"), (70, 4096, "<2,256>"), (65, 7168, "<4,256>"),
+                                      (70, 16384, "<8,256>"), (66, 32768, "<16,256>"), (66, 33024, "<0,256>"),
+                                      (4, 7168, "<1,1024>"), (4, 12288, "<2,1024>"), (2, 32768, "<4,1024>"),
+                                      (2, 65536, "<8,1024>"), (1, 66048, "<0,1024>")])
+def test_rmsnorm_quant_every_form(M, K, form):
+    rng = np.random.default_rng(M * 13 + K)
+    x = bf16(rng.standard_normal((M, K)) * 10.0 ** rng.integers(-3, 4, (M, 1)))
+    x[0, :128] = 0                                      # a zero group
+    g = bf16(rng.standard_normal(K) * 0.3 + 1.0)
+    check_rmsnorm(x, g, np.float32(1e-5), f"form {form}")
+
+
+def test_rmsnorm_quant_prefill_oproj_full_size():
+    """The bench's prefill case, 8191 x 7168 (256-thread form, 4 chunks per thread), in
+    one call; 256 seeded rows, the 8 zero tokens and the last row against the oracle
+    (each row is independent of the others)."""
+    wl = synth.WORKLOADS["prefill_oproj"]
+    x = synth.make_activation(wl)
+    g = bf16(oracle.bf16_bits_to_f32(synth.bf16_normal(1, wl.K, 0.1, wl.seed, synth.TID_GAMMA)[0]) + 1.0)
+    banner(f"rmsnorm_quant prefill_oproj full M={wl.M} K={wl.K}")
+    q, s = fb.rmsnorm_quant(dev_bf16(x), dev_bf16(g), 1e-5)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([synth.sample_rows(wl.M, 256, wl.seed), wl.zero_tokens(), [wl.M - 1]]))
+    rows_t = torch.from_numpy(rows.astype(np.int64)).cuda()
+    qh, sh = host_u8(q[rows_t]), host_f32(s[rows_t])
+    qo, so = oracle.rmsnorm_quant(x[rows], g, np.float32(1e-5))
+    assert_bits_equal(sh, so, "prefill_oproj rmsnorm scales")
+    assert_bits_equal(qh, qo, "prefill_oproj rmsnorm codes")
+    assert np.all(sh[np.isin(rows, wl.zero_tokens())] == 0)
 
 
 def test_rmsnorm_quant_redo_path():
