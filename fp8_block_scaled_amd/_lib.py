@@ -34,6 +34,7 @@ SIGNATURES = {
     "fp8_silu_mul_quant": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "fp8_rmsnorm_quant": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, _P, _I64, _I64, _P]),
     "fp8_block_linear": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    "fp8_block_linear_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "fp8_block_linear_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "nvfp4_w4a16_linear": (ctypes.c_int, [_P, _P, _P, ctypes.c_float, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "nvfp4_w4a16_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64]),

@@ -50,6 +50,32 @@ int quant_shape_check(const void* in, const void* q, const float* s, int64_t M, 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_HIP; }
 
+// Scratch of fp8_block_linear_noalloc: split-K partial sums (FP32 [split][M][N]),
+// written completely by the tile kernel before the reduce kernel reads them, so
+// nothing in it needs clearing between calls.  On a device of up to 256 CUs a split
+// keeps split x tiles <= 256 tiles of 128 x 128 partials, at most 16 MiB.  Each GPU
+// holds its own copy for the life of the process.  In host code `scratch` names a
+// host-side stand-in: kernels get the device address from hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = size_t{16} << 20;
+static_assert(kNoAllocScratchBytes == FP8BS_NOALLOC_SCRATCH_BYTES, "header and library disagree");
+__device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// The current device's scratch address, looked up once per device (with that device
+// current) and kept.
+int device_scratch(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FP8BS_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FP8BS_ERR_DEVICE;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FP8BS_ERR_HIP;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return FP8BS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -64,7 +90,9 @@ const char* fp8bs_status_string(int status) {
         case FP8BS_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte, scales 4-byte alignment)";
         case FP8BS_ERR_DEVICE: return "the current HIP device is not gfx950 (MI355X)";
         case FP8BS_ERR_HIP: return "HIP runtime call or kernel launch failed";
-        case FP8BS_ERR_WORKSPACE: return "workspace must be 256-byte aligned";
+        case FP8BS_ERR_WORKSPACE:
+            return "workspace must be 256-byte aligned (no-allocation call: the shape needs more than the static "
+                   "scratch)";
         case FP8BS_ERR_VALUE:
             return "scalar argument out of range (RMSNorm eps must be finite and > 0, the NVFP4 global scale finite)";
         default: return "unknown fp8bs status";
@@ -113,20 +141,24 @@ size_t fp8_block_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
     return fp8bs::prefill_workspace_size(M, N, K);     // split-K partial sums (0 when unused)
 }
 
-int fp8_block_linear(const void* q_e4m3, const float* s_f32, const void* w_e4m3, const float* ws_f32,
-                     void* y_bf16, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream) {
+namespace {
+
+int linear_check(const void* q_e4m3, const float* s_f32, const void* w_e4m3, const float* ws_f32, void* y_bf16,
+                 int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
     if (!mul_ok(N, K) || !mul_ok(M, K) || !mul_ok(M, N) || !mul_ok(M * N, 2)) return FP8BS_ERR_SHAPE;
-    if (M == 0 || N == 0) return FP8BS_OK;
+    if (M == 0 || N == 0) return 1;                      // nothing to do
     if (!q_e4m3 || !s_f32 || !w_e4m3 || !ws_f32 || !y_bf16) return FP8BS_ERR_NULL;
     if (!aligned(q_e4m3, 16) || !aligned(w_e4m3, 16) || !aligned(y_bf16, 16) || !aligned(s_f32, 4) ||
         !aligned(ws_f32, 4))
         return FP8BS_ERR_ALIGN;
-    if (workspace && !aligned(workspace, 256)) return FP8BS_ERR_WORKSPACE;
-    int cus = 0;
-    int rc = check_device(&cus);
-    if (rc != FP8BS_OK) return rc;
+    return FP8BS_OK;
+}
+
+// Schedule choice and launches of a validated call on a gfx950 device with `cus` CUs.
+int linear_dispatch(const void* q_e4m3, const float* s_f32, const void* w_e4m3, const float* ws_f32, void* y_bf16,
+                    int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, int cus,
+                    hipStream_t stream) {
     if (M <= fp8bs::kDecodeMaxM) {
         const fp8bs::DecodePlan plan = fp8bs::plan_decode(M, N, K, cus);
         return hip_status(
@@ -140,6 +172,31 @@ int fp8_block_linear(const void* q_e4m3, const float* s_f32, const void* w_e4m3,
     }
     return hip_status(fp8bs::launch_gemm_prefill(q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, cus, workspace,
                                                  workspace ? workspace_bytes : 0, stream));
+}
+
+}  // namespace
+
+int fp8_block_linear(const void* q_e4m3, const float* s_f32, const void* w_e4m3, const float* ws_f32,
+                     void* y_bf16, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+    int rc = linear_check(q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K);
+    if (rc != FP8BS_OK) return rc > 0 ? FP8BS_OK : rc;
+    if (workspace && !aligned(workspace, 256)) return FP8BS_ERR_WORKSPACE;
+    int cus = 0;
+    if ((rc = check_device(&cus)) != FP8BS_OK) return rc;
+    return linear_dispatch(q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, workspace, workspace_bytes, cus, stream);
+}
+
+int fp8_block_linear_noalloc(const void* q_e4m3, const float* s_f32, const void* w_e4m3, const float* ws_f32,
+                             void* y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    int rc = linear_check(q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K);
+    if (rc != FP8BS_OK) return rc > 0 ? FP8BS_OK : rc;
+    if (fp8_block_linear_workspace_size(M, N, K) > kNoAllocScratchBytes) return FP8BS_ERR_WORKSPACE;
+    int cus = 0;
+    if ((rc = check_device(&cus)) != FP8BS_OK) return rc;
+    void* ws = nullptr;
+    if ((rc = device_scratch(&ws)) != FP8BS_OK) return rc;
+    return linear_dispatch(q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, ws, kNoAllocScratchBytes, cus, stream);
 }
 
 int nvfp4_w4a16_linear(const void* x_bf16, const void* w_fp4, const void* bs_e4m3, float g, void* y_bf16,

@@ -43,7 +43,8 @@ typedef enum {
     FP8BS_ERR_ALIGN = -3,     /* a pointer violates the alignment rule above      */
     FP8BS_ERR_DEVICE = -4,    /* the current device is not gfx950                 */
     FP8BS_ERR_HIP = -5,       /* a HIP runtime call or a kernel launch failed     */
-    FP8BS_ERR_WORKSPACE = -6, /* workspace given but misaligned                   */
+    FP8BS_ERR_WORKSPACE = -6, /* workspace given but misaligned; or, without      */
+                              /* allocation, more scratch needed than the library holds */
     FP8BS_ERR_VALUE = -7      /* a scalar argument out of range (eps <= 0, non-finite g) */
 } fp8bs_status;
 
@@ -147,6 +148,24 @@ int fp8_block_linear(const void* q_e4m3, const float* s_f32,
                      void* y_bf16, int64_t M, int64_t N, int64_t K,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * fp8_block_linear for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and schedules as fp8_block_linear with a workspace of
+ * FP8BS_NOALLOC_SCRATCH_BYTES, except that the split-K partial sums go to a static
+ * device array inside the library (one per GPU, held until the process ends); the
+ * call allocates nothing.  The caller still passes inputs and outputs.  Shapes whose
+ * workspace size (fp8_block_linear_workspace_size) exceeds that array get
+ * FP8BS_ERR_WORKSPACE; on devices of up to 256 CUs no valid shape does.  Every call
+ * on one GPU shares its array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialized by the caller.  Nothing in the array needs
+ * clearing: each call writes every partial it reads.
+ */
+#define FP8BS_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int fp8_block_linear_noalloc(const void* q_e4m3, const float* s_f32,
+                             const void* w_e4m3, const float* ws_f32,
+                             void* y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 /* Bytes of workspace the fastest schedule of fp8_block_linear can use for this shape
  * on devices of up to 256 CUs (0 if none: M <= 32, and prefill shapes with enough
  * tiles; 0 for invalid shapes as well). */
@@ -199,7 +218,7 @@ const char* fp8bs_status_string(int status);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int fp8bs_abi_version(void);
 
-#define FP8BS_ABI_VERSION 10200
+#define FP8BS_ABI_VERSION 10300
 
 #ifdef __cplusplus
 }

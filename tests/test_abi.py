@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8bs_abi_version() == 10200
+    assert L.fp8bs_abi_version() == 10300
     for st in (OK, ENULL, ESHAPE, EALIGN, EDEV, EHIP, EWS, EVAL):
         assert L.fp8bs_status_string(st)
     assert b"unknown" in L.fp8bs_status_string(12345)
@@ -92,6 +92,21 @@ def test_block_linear_validation(L):
     assert f(A16, A16b, A16c, A16d, A16e, 4, 128, 128, A16 + 16, 4096, None) == EWS
     assert f(None, None, None, None, None, 0, 128, 128, None, 0, None) == OK     # M == 0
     assert f(None, None, None, None, None, 4, 0, 128, None, 0, None) == OK       # N == 0
+
+
+def test_block_linear_noalloc_validation(L):
+    f = L.fp8_block_linear_noalloc
+    assert f(A16, A16b, A16c, A16d, A16e, 4, 100, 128, None) == ESHAPE
+    assert f(A16, A16b, A16c, A16d, A16e, 4, 128, 0, None) == ESHAPE
+    assert f(A16, A16b, A16c, A16d, A16e, -4, 128, 128, None) == ESHAPE
+    assert f(None, A16b, A16c, A16d, A16e, 4, 128, 128, None) == ENULL
+    assert f(A16, A16b, A16c, A16d, None, 4, 128, 128, None) == ENULL
+    assert f(A16 + 4, A16b, A16c, A16d, A16e, 4, 128, 128, None) == EALIGN
+    assert f(A16, A16b, A16c, A16d + 2, A16e, 4, 128, 128, None) == EALIGN
+    assert f(None, None, None, None, None, 0, 128, 128, None) == OK     # M == 0
+    # The largest split-K workspace any valid shape asks for fits the static scratch.
+    for shape in ((33, 7168, 7168), (128, 7168, 7168), (100, 1024, 8192), (128, 16384, 7168), (200, 128, 8192)):
+        assert 0 < L.fp8_block_linear_workspace_size(*shape) <= 16 << 20, shape
 
 
 def test_nvfp4_linear_validation(L):
