@@ -79,6 +79,7 @@ def parse():
     p.add_argument("--workload", default="decode_qkv")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    p.add_argument("--no-ceilings", action="store_true", help="skip the measured stream-read and MFMA ceilings")
     p.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic.json"))
     p.add_argument("--make-traffic", metavar="DIR",
                    help="write --traffic-file from rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR "
@@ -99,7 +100,7 @@ def dev_bf16(bits):
 class Case:
     """Device-resident inputs and preallocated outputs of one linear workload."""
 
-    def __init__(self, wl, x_bits=None, gu_bits=None):
+    def __init__(self, wl, x_bits=None, gu_dev=None):
         import torch
         import fp8_block_scaled_amd as fb
         import synth
@@ -113,8 +114,8 @@ class Case:
         del wd
         self.qw = [qw] + [qw.clone() for _ in range(self.copies - 1)]
         self.ws = [ws] + [ws.clone() for _ in range(self.copies - 1)]
-        if gu_bits is not None:       # down projection: its input is SiLU(gate)*up of a gate/up tensor
-            self.gu = dev_bf16(gu_bits)
+        if gu_dev is not None:        # down projection: its input is SiLU(gate)*up of the gate/up output
+            self.gu = gu_dev
             self.x = None
         else:
             self.x = dev_bf16(x_bits if x_bits is not None else synth.make_activation(wl))
@@ -139,18 +140,30 @@ class Case:
         fb.block_linear(self.q, self.s, self.qw[c], self.ws[c], out=self.y, workspace=self.workspace)
 
 
-# Standard deviation of the gate/up output for x ~ N(0,1), W ~ N(0, 0.02^2), K = 7168.
-GU_SIGMA = 1.7
+def gate_up_output():
+    """The gate/up projection's output on the GPU, BF16 [8, 16384]: the spec_mlp_gu
+    workload's activations quantized and multiplied by its block-quantized weights.
+    The down projection's input is SiLU(gate)*up of this tensor, as in the model."""
+    import torch
+    import fp8_block_scaled_amd as fb
+    import synth
+    from synth import WORKLOADS
+    gw = WORKLOADS["spec_mlp_gu"]
+    q, s = fb.quant_act(dev_bf16(synth.make_activation(gw)))
+    wd = dev_bf16(synth.make_weight(gw))
+    qw, ws = fb.quant_weight(wd)
+    del wd
+    gu = fb.block_linear(q, s, qw, ws)
+    torch.cuda.synchronize()
+    del q, s, qw, ws
+    return gu
 
 
 def make_case(wl):
-    """A Case for workload ``wl``; the down projection takes SiLU(gate)*up of a seeded
-    gate/up tensor of the gate/up workload's output shape."""
-    import synth
-    from synth import WORKLOADS
+    """A Case for workload ``wl``; the down projection takes SiLU(gate)*up of the
+    gate/up projection's GPU output."""
     if wl.x_kind == "silu":
-        gw = WORKLOADS["spec_mlp_gu"]
-        return Case(wl, gu_bits=synth.bf16_normal(gw.M, gw.N, GU_SIGMA, gw.seed, synth.TID_GU))
+        return Case(wl, gu_dev=gate_up_output())
     return Case(wl)
 
 
@@ -480,17 +493,229 @@ def make_traffic(directory, out_path):
     print(json.dumps(doc, indent=1))
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The oracle, as it stands, on the same workload: quantize the activation row(s)
-    and dequantize-and-matmul in float64, repeated for about budget_s seconds."""
+_CEIL = None
+
+
+def ceil_lib():
+    """libfp8bs_ceilings.so: the measurement kernels (stream read, MFMA loop, clock)."""
+    global _CEIL
+    if _CEIL is None:
+        import ctypes
+        path = os.path.join(ROOT, "fp8_block_scaled_amd", "libfp8bs_ceilings.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m fp8_block_scaled_amd.build`")
+        lib = ctypes.CDLL(path)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.fp8bs_ceil_stream_read.argtypes = [P, I64, P, I, I, I, I, P]
+        lib.fp8bs_ceil_stream_read.restype = I
+        lib.fp8bs_ceil_mfma.argtypes = [I, I, I, P, P, P]
+        lib.fp8bs_ceil_mfma.restype = I
+        lib.fp8bs_ceil_wallclock_khz.argtypes = []
+        lib.fp8bs_ceil_wallclock_khz.restype = I
+        _CEIL = lib
+    return _CEIL
+
+
+STREAM_CONFIGS = [(wgs, threads, unroll, nt) for wgs in (256, 512, 1024, 2048) for threads in (256, 512, 1024)
+                  for unroll in (4, 8) for nt in (0, 1)]
+
+
+def stream_ceiling(nbytes, copies, steps=100):
+    """The best rate of a plain streaming read of ``nbytes`` (each launch reads one of
+    ``copies`` buffers in turn, so the Infinity Cache cannot serve them), over the
+    launch shapes of STREAM_CONFIGS, graph-timed like the GEMMs.  The read kernel
+    moves exactly ``nbytes`` per launch."""
+    import torch
+    lib = ceil_lib()
+    n = (nbytes + 15) // 16 * 16
+    bufs = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.empty(2048 * 1024, dtype=torch.int32, device="cuda")
+    best = None
+    for cfg in STREAM_CONFIGS:
+        def launch(i):
+            rc = lib.fp8bs_ceil_stream_read(bufs[i % copies].data_ptr(), n, sink.data_ptr(), *cfg,
+                                            torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"stream read launch failed ({rc})")
+        for i in range(3):
+            launch(i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                launch(i)
+        graph.replay()
+        us = _replay_ms(graph) * 1e3 / steps
+        del graph
+        if best is None or us < best[0]:
+            best = (us, cfg)
+    del bufs, sink
+    torch.cuda.empty_cache()
+    us, (wgs, threads, unroll, nt) = best
+    return {"bytes": n, "us": round(us, 2), "GB/s": round(n / (us * 1e-6) / 1e9, 1), "copies_rotated": copies,
+            "launch": {"workgroups": wgs, "threads": threads, "loads_in_flight_per_lane": unroll,
+                       "nontemporal": bool(nt)}}
+
+
+def mfma_ceiling(promote, wgs=512, iters=2000):
+    """FP8 MFMA rate of a register-only loop (8 chains of v_mfma_f32_16x16x128_f8f6f4
+    per wave, 2 waves per SIMD), and the shader clock it ran at (s_memtime over
+    s_memrealtime).  With ``promote`` every MFMA starts from zero and is folded into
+    FP32 accumulators by four FMAs, the GEMM's promotion per K block."""
+    import torch
+    lib = ceil_lib()
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        if lib.fp8bs_ceil_mfma(wgs, iters, int(promote), out.data_ptr(), clk.data_ptr(), st) != 0:
+            raise RuntimeError("MFMA loop launch failed")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        lib.fp8bs_ceil_mfma(wgs, iters, int(promote), out.data_ptr(), clk.data_ptr(), st)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    flops = wgs * 4 * iters * 8 * 65536
+    ticks, real = (int(v) for v in clk.cpu().tolist())
+    khz = lib.fp8bs_ceil_wallclock_khz()
+    clock_ghz = ticks / (real / (khz * 1e3)) / 1e9 if real > 0 and khz > 0 else None
+    tflops = flops / (us * 1e-6) / 1e12
+    r = {"TFLOP/s": round(tflops, 1), "us": round(us, 1), "flop": flops,
+         "shader_clock_GHz": round(clock_ghz, 3) if clock_ghz else None,
+         "frac_of_5000": round(tflops / FP8_PEAK_TFLOPS, 4)}
+    if clock_ghz:
+        # Dense FP8 peak at the clock observed: 256 CUs x 8192 flop per clock.
+        r["peak_at_observed_clock_TFLOP/s"] = round(256 * 8192 * clock_ghz * 1e9 / 1e12, 1)
+    return r
+
+
+def smi_snapshot():
+    """amd-smi's clock and power readings for GPU 0 at this moment (None if unavailable)."""
+    import subprocess
+    try:
+        p = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"],
+                           capture_output=True, text=True, timeout=30)
+        if p.returncode != 0:
+            return None
+        d = json.loads(p.stdout)
+    except Exception:
+        return None
+    d = d[0] if isinstance(d, list) and d else d
+    if isinstance(d, dict) and "gpu_data" in d:
+        d = d["gpu_data"][0] if d["gpu_data"] else d
+    out = {}
+    pw = d.get("power", {}) if isinstance(d, dict) else {}
+    for k in ("socket_power", "current_socket_power", "average_socket_power"):
+        if isinstance(pw.get(k), dict) and "value" in pw[k]:
+            out["power_W"] = pw[k]["value"]
+            break
+    ck = d.get("clock", {}) if isinstance(d, dict) else {}
+    for k in ("gfx_0", "GFX_0", "gfx"):
+        if isinstance(ck.get(k), dict):
+            c = ck[k].get("clk", ck[k])
+            out["gfx_clock_MHz"] = c.get("value") if isinstance(c, dict) else c
+            break
+    mem = ck.get("mem_0") if isinstance(ck, dict) else None
+    if isinstance(mem, dict):
+        c = mem.get("clk", mem)
+        out["mem_clock_MHz"] = c.get("value") if isinstance(c, dict) else c
+    return out or None
+
+
+def cpu_env():
+    """Host cores this process may use, the CPU model, and the BLAS thread count the
+    oracle's float64 matmul is given: the cores, capped at 16 (one GPU's share of the
+    host), set explicitly through threadpoolctl and recorded."""
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    blas = max(1, min(16, cores))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cores": cores, "blas_threads": blas, "cpu_model": model}
+
+
+def _timing_weights(wl):
+    """Weight codes and block scales of ``wl``'s shape for timing the oracle: codes drawn
+    uniformly over the finite E4M3 bytes, scales over [1e-4, 1e-3).  The weights'
+    block quantization is the offline step (untimed on both sides), and the oracle's
+    dequantize-and-matmul costs the same for any values."""
     import numpy as np
+    rng = np.random.default_rng(wl.seed)
+    qw = rng.integers(0, 256, (wl.N, wl.K), dtype=np.uint8)
+    qw[(qw & 0x7F) == 0x7F] ^= 1                  # no NaN codes
+    ws = rng.uniform(1e-4, 1e-3, (wl.N // 128, wl.K // 128)).astype(np.float32)
+    return qw, ws
+
+
+def _oracle_step(wl, rows, qw, ws):
+    """One pass of the oracle over ``rows`` of workload ``wl``: quantize the rows'
+    activations (the down projection: SiLU(gate)*up of a gate/up tensor of N(0, 1.7^2),
+    then quantize) and dequantize-and-multiply in float64.  Returns seconds."""
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = 1
+    from synth import WORKLOADS
+    if wl.x_kind == "silu":
+        gw = WORKLOADS["spec_mlp_gu"]
+        gu = synth.bf16_normal(len(rows), gw.N, 1.7, gw.seed, synth.TID_GU)
+        x = None
+    else:
+        x = synth.activation_rows(wl, rows)
+    t0 = time.perf_counter()
+    q, s = oracle.silu_mul_quant(gu) if x is None else oracle.quant_act(x)
+    oracle.linear_ref(q, s, qw, ws)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline_per_config(env):
+    """The oracle on every workload: in full for the decode shapes, on a few hundred
+    rows for the prefill shapes, with a labelled linear extrapolation t(M) = a + b M
+    fitted from two row counts (the weights are dequantized once per call, a fixed
+    cost; quantization and the matmul grow with the rows)."""
+    import numpy as np
+    from synth import WORKLOADS
+    out = {}
+    for name in ("tiny", "decode_qkv", "spec_mlp_gu", "spec_mlp_down", "prefill_oproj", "fusion_fc"):
+        wl = WORKLOADS[name]
+        print(f"[bench] cpu baseline (oracle): {name}", file=sys.stderr, flush=True)
+        qw, ws = _timing_weights(wl)
+        if wl.M <= 16:
+            reps = 3 if wl.M * wl.N * wl.K < 1e9 else 1
+            t = min(_oracle_step(wl, np.arange(wl.M), qw, ws) for _ in range(reps))
+            out[name] = {"rows": wl.M, "s": round(t, 4), "GB/s": round((wl.quant_bytes() + wl.gemm_bytes()) / t / 1e9, 4),
+                         "GFLOP/s": round(wl.gemm_flops() / t / 1e9, 2), "timed": "full call"}
+        else:
+            r1, r2 = 64, 256
+            _oracle_step(wl, np.arange(16), qw, ws)          # untimed: first-touch costs
+            t1 = _oracle_step(wl, np.arange(r1), qw, ws)
+            t2 = _oracle_step(wl, np.arange(r2), qw, ws)
+            b = max((t2 - t1) / (r2 - r1), 1e-12)
+            a = max(t1 - b * r1, 0.0)
+            full = a + b * wl.M
+            out[name] = {"rows": [r1, r2], "s": [round(t1, 4), round(t2, 4)],
+                         "s_per_row": round(b, 6), "fixed_s": round(a, 4),
+                         "extrapolated_full_M_s": round(full, 2),
+                         "extrapolated_GFLOP/s": round(wl.gemm_flops() / full / 1e9, 2),
+                         "timed": f"rows 0..{r1 - 1} and 0..{r2 - 1}; full M={wl.M} is a linear extrapolation"}
+        del qw, ws
+    out["weights"] = "E4M3 codes drawn uniformly (finite codes), scales uniform: the offline quantization is untimed"
+    return out
+
+
+def cpu_baseline(wl, env, budget_s=12.0):
+    """The oracle, as it stands, on the same workload: quantize the activation row(s)
+    and dequantize-and-matmul in float64, repeated for about budget_s seconds."""
+    import synth
+    import oracle
     x = synth.make_activation(wl)
     w = synth.make_weight(wl)
     qw, ws = oracle.quant_weight(w)            # offline step, untimed as on the GPU
@@ -504,11 +729,11 @@ def cpu_baseline(wl, budget_s=12.0):
             break
     per_step = el / reps
     bytes_step = wl.quant_bytes() + wl.gemm_bytes()
-    return {"value": round(bytes_step / per_step / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
-            "kind": "oracle",
+    return {"value": round(bytes_step / per_step / 1e9, 4), "unit": "GB/s", "cores": env["blas_threads"],
+            "kind": "oracle", "cpu_model": env["cpu_model"], "cores_available": env["cores"],
             "sample": (f"{reps} full steps of {wl.name} (M={wl.M}, K={wl.K}, N={wl.N}): numpy quantizer "
-                       f"(1 thread) + float64 dequantize-and-matmul (BLAS, {blas_threads} threads), "
-                       f"{el:.1f} s, {per_step * 1e3:.1f} ms/step")}
+                       f"(1 thread) + float64 dequantize-and-matmul (BLAS, {env['blas_threads']} threads set "
+                       f"through threadpoolctl), {el:.1f} s, {per_step * 1e3:.1f} ms/step")}
 
 
 def summarize_rocprof(directory):
@@ -608,8 +833,28 @@ def main():
         "roofline": roofline_for(wl, gemm_us, traffic),
         "kernels_us": {"block_linear": round(gemm_us, 2), "quant_act": round(quant_us, 2)},
     }
+    out["smi_after_headline"] = smi_snapshot()
     del case
     torch.cuda.empty_cache()
+
+    if not args.no_ceilings:
+        # Measured ceilings next to the published peaks: a plain streaming read at each
+        # decode workload's byte count (same rotation as its weights), and the FP8 MFMA
+        # loop alone and with the promotion FMAs.
+        print("[bench] ceilings", file=sys.stderr, flush=True)
+        ceil = {"stream_read": {}}
+        for name in ("decode_qkv", "spec_mlp_gu", "spec_mlp_down"):
+            w2 = WORKLOADS[name]
+            copies = max(1, min(16, -(-2 * MALL_BYTES // (w2.N * w2.K))))
+            ceil["stream_read"][name] = stream_ceiling(w2.gemm_bytes(), copies)
+        ceil["mfma_fp8"] = mfma_ceiling(False)
+        ceil["mfma_fp8_with_promotion"] = mfma_ceiling(True)
+        ceil["smi"] = smi_snapshot()
+        out["ceilings"] = ceil
+        sr = ceil["stream_read"].get(wl.name)
+        if sr and out["roofline"]["bound"] == "hbm":
+            out["roofline"]["measured_stream_ceiling_GB/s"] = sr["GB/s"]
+            out["roofline"]["frac_of_measured_ceiling"] = round(out["roofline"]["achieved"] / sr["GB/s"], 4)
 
     if not args.no_others:
         others = {}
@@ -626,9 +871,24 @@ def main():
             others[name] = {"M": w2.M, "K": w2.K, "N": w2.N, "ms_per_step": round(ms2, 5),
                             "block_linear_us": round(g2, 2), "quant_us": round(q2, 2),
                             "gemm_roofline": rl, "weight_copies_rotated": c2.copies}
+            if w2.x_kind == "silu":
+                others[name]["input"] = "SiLU(gate)*up of the gate/up projection's GPU output, re-quantized"
+            if w2.M > 16:
+                others[name]["smi_after"] = smi_snapshot()
             del c2
             torch.cuda.empty_cache()
         out["workloads"] = others
+        ceil = out.get("ceilings")
+        if ceil:
+            for name, ent in others.items():
+                rl = ent["gemm_roofline"]
+                sr = ceil["stream_read"].get(name)
+                if rl["bound"] == "hbm" and sr:
+                    rl["measured_stream_ceiling_GB/s"] = sr["GB/s"]
+                    rl["frac_of_measured_ceiling"] = round(rl["achieved"] / sr["GB/s"], 4)
+                elif rl["bound"] == "mfma":
+                    for key in ("mfma_fp8", "mfma_fp8_with_promotion"):
+                        rl[f"frac_of_{key}_loop"] = round(rl["achieved"] / ceil[key]["TFLOP/s"], 4)
         print("[bench] M sweep", file=sys.stderr, flush=True)
         out["m_sweep"] = time_m_sweep()
         out["w4a16"] = time_w4_all(args.steps, args.traffic_file)
@@ -641,7 +901,16 @@ def main():
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl)
+        env = cpu_env()
+        try:
+            from threadpoolctl import threadpool_limits
+            limiter = threadpool_limits(limits=env["blas_threads"])
+        except Exception:  # pragma: no cover
+            limiter = None
+        out["cpu_baseline"] = cpu_baseline(wl, env)
+        if not args.no_others:
+            out["cpu_baseline_per_config"] = cpu_baseline_per_config(env)
+        del limiter
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -65,6 +65,14 @@ constexpr int prefill_lds_bytes(int BM, int BN) { return 2 * stage_bytes(BM, BN)
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
+// acc += sc * p: the promotion of one 16 x 16 K-block product into its accumulators.
+__device__ __forceinline__ void promote(v4f& acc, float sc, const v4f& p) {
+    acc[0] = fmaf(sc, p[0], acc[0]);
+    acc[1] = fmaf(sc, p[1], acc[1]);
+    acc[2] = fmaf(sc, p[2], acc[2]);
+    acc[3] = fmaf(sc, p[3], acc[3]);
+}
+
 __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int g) {
     const v4i lo = *reinterpret_cast<const v4i*>(tile + swz(row, g));
     const v4i hi = *reinterpret_cast<const v4i*>(tile + swz(row, g + 4));
@@ -234,35 +242,58 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
     copy_wscales(kb0, 0);
     warm(kb0 + 1 < kb1 ? kb0 + 1 : kb1 - 1);
 
-    for (int64_t kb = kb0; kb < kb1; ++kb) {
-        const int stage = (int)((kb - kb0) & 1);
-        // This wave's copies into `stage` (and the scale loads) have landed -- all
-        // but the last load issued, the warm-up touch; the barrier makes everyone's
-        // copies visible and frees the other stage.
-        // A plain s_barrier: __syncthreads() would add a full vmcnt(0) wait (its
-        // fence) and so wait for the warm-up touch as well.  Every LDS read of the
-        // previous step was consumed before a wave reaches the barrier, and each
-        // wave has waited for its own copies above; the empty asm statements keep
-        // the compiler from moving LDS accesses across the barrier.
-        asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        const bool more = kb + 1 < kb1;
-        const uint8_t* wt = lds + stage * kStage;
+    // Fragments of one step, read from LDS stage `st`: the TJ B fragments (token rows),
+    // their promotion factors s[m] * ws[nb], and the first A fragment (weight rows).
+    v8i bf[TJ], af_next;
+    float xsv[TJ], wsc = 0.0f;
+    auto load_frags = [&](int st) {
+        const uint8_t* wt = lds + st * kStage;
         const uint8_t* xt = wt + BN * 128;
-        v8i bf[TJ];
+        // Scales first: LDS reads return in order, so their wait does not include the
+        // fragments issued after them.
+        const float* xs_lds = reinterpret_cast<const float*>(xt + BM * 128);
+        wsc = reinterpret_cast<const float*>(xt + BM * 128 + BM * 4)[(wn * WTN) / kGroup];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) xsv[j] = xs_lds[wm * WTM + 16 * j + r];
 #pragma unroll
         for (int j = 0; j < TJ; ++j) bf[j] = lds_frag(xt, wm * WTM + 16 * j + r, g);
-        const float* xs_lds = reinterpret_cast<const float*>(xt + BM * 128);
-        const float wsc = reinterpret_cast<const float*>(xt + BM * 128 + BM * 4)[(wn * WTN) / kGroup];
-        float sc[TJ];
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) sc[j] = xs_lds[wm * WTM + 16 * j + r] * wsc;
-        // Subtile row i: TJ independent MFMAs (own result registers), then their
-        // promotions; the next A fragment is read from LDS meanwhile.
-        v8i af_next = lds_frag(wt, wn * WTN + r, g);
+        af_next = lds_frag(wt, wn * WTN + r, g);
+    };
+    // This wave's copies into a stage (and the scale loads) have landed -- all but the
+    // last load issued, the warm-up touch; the barrier makes everyone's copies
+    // visible.  A plain s_barrier: __syncthreads() would add a full vmcnt(0) wait (its
+    // fence) and so wait for the warm-up touch as well.  Each wave has consumed every
+    // LDS read of the other stage (lgkmcnt) and waited for its own copies; the empty
+    // asm statements keep the compiler from moving LDS accesses across the barrier.
+    auto stage_ready = [&]() {
+        asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    stage_ready();
+    load_frags(0);
+
+    for (int64_t kb = kb0; kb < kb1; ++kb) {
+        const int stage = (int)((kb - kb0) & 1);
+        const bool more = kb + 1 < kb1;
+        const uint8_t* wt = lds + stage * kStage;
+        // Subtile row i: TJ independent MFMAs (own result registers), each followed by
+        // the promotion of row i - 1's result in the same column (one row later than it
+        // was issued, so the FMAs do not wait for the MFMA pipe); the next A fragment is
+        // read from LDS meanwhile.  After the last row's MFMAs are issued, the workgroup
+        // meets at the barrier for the next stage and reads the next step's fragments
+        // while those MFMAs run and the last row is promoted: the step boundary does not
+        // drain the MFMA pipe.
+        v4f pend[TJ];
+        float sc[TJ];                                   // promotion factors s[m] * ws[nb]
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
+            // Formed where first needed (row 1's promotions), past the wait for row 0's
+            // fragments, so the scale reads add no wait of their own.
+            if (i == (TI > 1 ? 1 : 0)) {
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) sc[j] = xsv[j] * wsc;
+            }
             // The copies of K block kb + 1 are spread over the first rows, so the
             // workgroup's vector-memory requests do not queue up at the top of the
             // step in front of its LDS reads; past the last K block they repeat it
@@ -279,21 +310,31 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
             }
             const v8i af = af_next;
             if (i + 1 < TI) af_next = lds_frag(wt, wn * WTN + 16 * (i + 1) + r, g);
-            v4f p[TJ];
 #pragma unroll
             for (int j = 0; j < TJ; ++j) {
                 const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
                 // Format 0 = E4M3 for both operands; zero scale operands select the unscaled MFMA.
-                p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], zero, 0, 0, 0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-                acc[i][j][0] = fmaf(sc[j], p[j][0], acc[i][j][0]);
-                acc[i][j][1] = fmaf(sc[j], p[j][1], acc[i][j][1]);
-                acc[i][j][2] = fmaf(sc[j], p[j][2], acc[i][j][2]);
-                acc[i][j][3] = fmaf(sc[j], p[j][3], acc[i][j][3]);
+                const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], zero, 0, 0, 0, 0, 0, 0);
+                // The promotion of the previous row's subtile j, TJ MFMAs after it was issued:
+                // its result is ready, so the FMAs run while this row's MFMAs execute.  The
+                // scheduling barriers keep the compiler from moving FMAs next to the MFMA
+                // whose result they read.
+                __builtin_amdgcn_sched_barrier(0);
+                if (i > 0) promote(acc[i - 1][j], sc[j], pend[j]);
+                __builtin_amdgcn_sched_barrier(0);
+                pend[j] = p;
             }
         }
+        float sc_last[TJ];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) sc_last[j] = sc[j];
+        // Past the last K block the other stage holds a repeat of this one: reading it
+        // keeps the loop free of branches (a branch here would keep both fragment sets
+        // alive across it).
+        stage_ready();
+        load_frags(stage ^ 1);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) promote(acc[TI - 1][j], sc_last[j], pend[j]);
     }
 
     // No direct-to-LDS load (the last warm-up touch) may still be in flight when
