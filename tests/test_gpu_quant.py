@@ -130,6 +130,21 @@ def test_silu_mul_quant_both_sides_of_the_unrolled_form(M, I):
     assert_bits_equal(host_u8(q), qo, "silu codes")
 
 
+@pytest.mark.parametrize("M,I", [(65537, 128), (65600, 256)])
+def test_silu_mul_quant_rows_past_the_grid(M, I):
+    """More rows than the grid's second dimension holds (65,535): blocks walk the rest with a
+    stride; every row, the last ones included, bit-exact."""
+    rng = np.random.default_rng(M + 3 * I)
+    gu = bf16(rng.standard_normal((M, 2 * I)) * 1.7)
+    gu[-1, :4] = bf16(np.array([3.0, -2.0, 0.5, 80.0], np.float32))
+    banner(f"silu_mul_quant M={M} I={I} (rows past the grid)")
+    q, s = fb.silu_mul_quant(dev_bf16(gu))
+    torch.cuda.synchronize()
+    qo, so = oracle.silu_mul_quant(gu)
+    assert_bits_equal(host_f32(s), so, "silu scales")
+    assert_bits_equal(host_u8(q), qo, "silu codes")
+
+
 def test_quant_is_deterministic():
     rng = np.random.default_rng(99)
     x = dev_bf16(bf16(rng.standard_normal((257, 2048))))
