@@ -11,12 +11,12 @@
 //      and the workgroup meets at a barrier; the copies of K block kb + 1 into the
 //      other stage are then issued, two per subtile row over the first rows --
 //      direct global -> LDS loads (global_load_lds_dwordx4: no VGPRs, no LDS write
-//      instructions), overlapping the compute of step kb.  Each thread also
-//      touches one 128-byte line of K block kb + 2 (a 4-byte direct-to-LDS load
-//      into a dump area) so that the copies of the next step find their lines in
-//      L2: a double-buffered 256 x 256 tile fills 128 KB of LDS, leaving no room
-//      for a third stage, and the first touch of a line from HBM takes longer
-//      than one step of compute;
+//      instructions), overlapping the compute of step kb.  With 128 x 256 tiles each
+//      thread also touches one 128-byte line of K block kb + 2 (a 4-byte
+//      direct-to-LDS load into a dump area) so that the next copies find their
+//      lines in L2; measured with this schedule, the touch pays for that shape
+//      (M = 768 on the 7168 x 7168 projection: 85 against 93 us) and costs 2-8%
+//      on the others (its memory instructions outweigh the L2 misses they save);
 //   2. each wave runs v_mfma_f32_16x16x128_f8f6f4 over its 16 x 16 subtiles (A = 16
 //      weight rows, B = 16 token rows; one MFMA covers the whole K block) and folds
 //      each FP32 result into its accumulators with acc += (s[m] * ws[nb]) * P: the
@@ -60,8 +60,10 @@ struct PrefillArgs {
 // Bytes of one LDS stage: w tile, q tile, BM token scales, weight scales (one
 // wave's 4-byte copy writes 256 bytes; the first BN/128 are the tile's weight blocks).
 constexpr int stage_bytes(int BM, int BN) { return (BM + BN) * 128 + BM * 4 + 256; }
-// Dynamic LDS of a launch: two stages and the 256-byte warm-up dump.
-constexpr int prefill_lds_bytes(int BM, int BN) { return 2 * stage_bytes(BM, BN) + 256; }
+// Tile shapes whose K loop touches the lines of K block kb + 2 ahead of the copies.
+constexpr bool prefill_warm(int BM, int BN) { return BM == 128 && BN == 256; }
+// Dynamic LDS of a launch: two stages, plus the 256-byte dump of the warm-up touches.
+constexpr int prefill_lds_bytes(int BM, int BN) { return 2 * stage_bytes(BM, BN) + (prefill_warm(BM, BN) ? 256 : 0); }
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
@@ -181,9 +183,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
         for (int c = 0; c < kCopies; ++c) copy_one(kb, stage, c);
     };
 
-    // ---- L2 warm-up of K block kb + 2: thread t touches stage row t mod (BM + BN)
-    // (one line).  Every thread issues it, so it is always each wave's last load.
-    static_assert(BM + BN <= kThreads, "one warm-up line per thread covers the stage");
+    // ---- L2 warm-up of K block kb + 2 (WARM shapes): thread t touches stage row
+    // t mod (BM + BN) (one line), always as each wave's last vector load.
+    constexpr bool WARM = prefill_warm(BM, BN);
+    static_assert(!WARM || BM + BN <= kThreads, "one warm-up line per thread covers the stage");
     const int pf_row = tid % (BM + BN);
     const bool pf_w = pf_row < BN;
     int64_t pf_off;
@@ -193,14 +196,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
         pf_off = row * a.K;
     }
     auto warm = [&](int64_t kb) {
-        const uint8_t* base = (pf_w ? a.w : a.x) + kb * kGroup;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + pf_off),
-                                         (__attribute__((address_space(3))) void*)(lds + 2 * kStage), 4, 0, 0);
+        if constexpr (WARM) {
+            const uint8_t* base = (pf_w ? a.w : a.x) + kb * kGroup;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + pf_off),
+                                             (__attribute__((address_space(3))) void*)(lds + 2 * kStage), 4, 0, 0);
+        }
     };
 
     // ---- scales: the BM token scales and the weight-block scales of K block kb are
-    // copied into the stage with the tiles (4-byte direct-to-LDS loads), so the
-    // warm-up touch is always each wave's last vector load and nothing waits on it.
+    // copied into the stage with the tiles (4-byte direct-to-LDS loads).
     static_assert(BM % 64 == 0 && BM / 64 <= kWaves, "one scale copy per wave");
     const bool xs_copy = wave < BM / 64;
     uint32_t xs_off;
@@ -259,14 +263,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
         for (int j = 0; j < TJ; ++j) bf[j] = lds_frag(xt, wm * WTM + 16 * j + r, g);
         af_next = lds_frag(wt, wn * WTN + r, g);
     };
-    // This wave's copies into a stage (and the scale loads) have landed -- all but the
-    // last load issued, the warm-up touch; the barrier makes everyone's copies
-    // visible.  A plain s_barrier: __syncthreads() would add a full vmcnt(0) wait (its
-    // fence) and so wait for the warm-up touch as well.  Each wave has consumed every
-    // LDS read of the other stage (lgkmcnt) and waited for its own copies; the empty
-    // asm statements keep the compiler from moving LDS accesses across the barrier.
+    // This wave's copies into a stage (and the scale loads) have landed -- with the
+    // warm-up, all but the last load issued, the touch -- and it has consumed every
+    // LDS read of the other stage; the barrier makes everyone's copies visible.  A
+    // plain s_barrier: __syncthreads() would add a full vmcnt(0) wait (its fence).  The
+    // empty asm statements keep the compiler from moving LDS accesses across it.
     auto stage_ready = [&]() {
-        asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)" ::: "memory");
+        if constexpr (WARM)
+            asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
             if (i == kCopyRows - 1) {
                 copy_scales(kn, stage ^ 1);
                 copy_wscales(kn, stage ^ 1);
-                warm(kb + 2 < kb1 ? kb + 2 : kb1 - 1);         // always one warm-up load last
+                warm(kb + 2 < kb1 ? kb + 2 : kb1 - 1);         // with WARM, always one touch last
             }
             const v8i af = af_next;
             if (i + 1 < TI) af_next = lds_frag(wt, wn * WTN + 16 * (i + 1) + r, g);
