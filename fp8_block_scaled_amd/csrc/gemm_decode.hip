@@ -25,7 +25,8 @@
 //   * Each workgroup owns NS adjacent strips; each wave loads one activation
 //     fragment per super block and uses it for the NS strips' MFMAs.  Every
 //     workgroup reads the whole M x K activation codes (from L2), so NS trades
-//     activation traffic against the number of workgroups.
+//     activation traffic against the number of workgroups; it is chosen per shape
+//     so that every CU receives as nearly the same number of strips as possible.
 //   * Each lane requests the fragments and scales of CH super blocks at a time.
 //     The weight scale index is made wave-uniform.
 //
@@ -46,11 +47,11 @@ namespace fp8bs {
 
 constexpr int kDecodeMaxWaves = 16;
 // Workgroup shape, from measurement on the decode shapes (M = 1 and 8, K = 7168
-// and 8192, N = 7168..16384): 8 waves per workgroup and 2 strips per workgroup
-// gave the shortest times; fewer waves leave a CU short of loads in flight, more
-// strips per workgroup leave too few workgroups to spread evenly over the CUs.
+// and 8192, N = 7168..16384): 8 waves per workgroup; fewer leave a CU short of
+// loads in flight.  Strips per workgroup (1..4) are chosen per shape in
+// plan_decode.
 constexpr int kWavesPerWg = 8;
-constexpr int kStripsPerWg = 2;
+constexpr int kMaxStripsPerWg = 4;
 
 struct DecodeArgs {
     const uint8_t* w;
@@ -63,10 +64,9 @@ struct DecodeArgs {
     int64_t strips;                          // N / P
 };
 
-template <int P, int NS>
+template <int P, int NS, int CH>
 __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(DecodeArgs a) {
     constexpr int G = 16 / P;
-    constexpr int CH = NS <= 2 ? 2 : 1;      // super blocks per load batch
     extern __shared__ __attribute__((aligned(16))) v4f red[];      // [S][NS][64] partial sums
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -91,15 +91,18 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
         wsrow[q] = a.ws + ((st * P) / kGroup) * a.KB;
     }
 
-    // A batch: fragments and scales of up to CH super blocks, requested before any
-    // is used.  Branch-free: K blocks past KB (a last, partial super block) are
-    // clamped to valid addresses and zeroed at use.
+    // A batch: fragments and scales of CH super blocks, all requested before any is
+    // used.  Branch-free, so that no load is sunk past another super block's MFMAs:
+    // a super block past the wave's range re-reads the wave's last one, a K block
+    // past KB (a last, partial super block) is clamped to the last K block, and both
+    // are zeroed at use.
     v4i wv[CH][NS][2], xv[CH][2];
     float xsv[CH], wsv[CH][NS];
     auto load_batch = [&](int64_t sb) {
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            int64_t k = (sb + i) * G + tb;
+            const int64_t sbi = sb + i < sb1 ? sb + i : sb1 - 1;
+            int64_t k = sbi * G + tb;
             k = k < a.KB ? k : a.KB - 1;
             const v4i* xp = reinterpret_cast<const v4i*>(xrow + k * kGroup);
             xv[i][0] = xp[0];
@@ -122,25 +125,24 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
     const v4i z4 = {0, 0, 0, 0};
     for (int64_t sb = sb0; sb < sb1; sb += CH) {
         load_batch(sb);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            if (sb + i < sb1) {                                  // uniform
-                const bool use = mvalid && (sb + i) * G + tb < a.KB;
-                const v4i b0 = use ? xv[i][0] : z4, b1 = use ? xv[i][1] : z4;
-                const v8i bv = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-                const float xsc = use ? xsv[i] : 0.0f;
+            const bool use = mvalid && sb + i < sb1 && (sb + i) * G + tb < a.KB;
+            const v4i b0 = use ? xv[i][0] : z4, b1 = use ? xv[i][1] : z4;
+            const v8i bv = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            const float xsc = use ? xsv[i] : 0.0f;
 #pragma unroll
-                for (int q = 0; q < NS; ++q) {
-                    const v8i av = {wv[i][q][0].x, wv[i][q][0].y, wv[i][q][0].z, wv[i][q][0].w,
-                                    wv[i][q][1].x, wv[i][q][1].y, wv[i][q][1].z, wv[i][q][1].w};
-                    // Format 0 = E4M3 for both operands; zero scale operands select the unscaled MFMA.
-                    const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, zero, 0, 0, 0, 0, 0, 0);
-                    const float sc = xsc * wsv[i][q];
-                    acc[q][0] = fmaf(sc, p[0], acc[q][0]);
-                    acc[q][1] = fmaf(sc, p[1], acc[q][1]);
-                    acc[q][2] = fmaf(sc, p[2], acc[q][2]);
-                    acc[q][3] = fmaf(sc, p[3], acc[q][3]);
-                }
+            for (int q = 0; q < NS; ++q) {
+                const v8i av = {wv[i][q][0].x, wv[i][q][0].y, wv[i][q][0].z, wv[i][q][0].w,
+                                wv[i][q][1].x, wv[i][q][1].y, wv[i][q][1].z, wv[i][q][1].w};
+                // Format 0 = E4M3 for both operands; zero scale operands select the unscaled MFMA.
+                const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, zero, 0, 0, 0, 0, 0, 0);
+                const float sc = xsc * wsv[i][q];
+                acc[q][0] = fmaf(sc, p[0], acc[q][0]);
+                acc[q][1] = fmaf(sc, p[1], acc[q][1]);
+                acc[q][2] = fmaf(sc, p[2], acc[q][2]);
+                acc[q][3] = fmaf(sc, p[3], acc[q][3]);
             }
         }
     }
@@ -150,9 +152,10 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
     __syncthreads();
     // Output (m, c) of strip q: sum over waves, then over the G groups, of the
     // diagonal-block entry C[t P + c][t P + m], held by lane 16 ((t P + c) / 4) +
-    // t P + m in its component c % 4.
-    if (wave == 0) {
-        for (int o = lane; o < NS * a.M * P; o += 64) {
+    // t P + m in its component c % 4.  Every thread of the workgroup takes outputs:
+    // each output is still summed by one thread in a fixed order.
+    {
+        for (int o = threadIdx.x; o < NS * a.M * P; o += blockDim.x) {
             const int q = o / (a.M * P), rem = o % (a.M * P);
             const int m = rem / P, c = rem % P;
             if (strip0 + q >= a.strips) continue;
@@ -172,16 +175,36 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
 // Row-group size for M tokens: the smallest of 4, 8, 16 that holds them.
 static int choose_rows(int64_t M) { return M <= 4 ? 4 : (M <= 8 ? 8 : 16); }
 
+// Strips per workgroup.  The workgroups are spread round-robin over the CUs and a
+// CU's own bandwidth is limited, so the time follows the most strips any CU
+// receives: ceil(workgroups / cus) * NS.  Take the NS that makes it smallest, and
+// of equals the largest (fewer workgroups, fewer re-reads of the activations).
+// Measured at M = 1, N = 9216, K = 7168 (2304 strips of 4): NS = 3 (9 strips on
+// every CU) 13.4 us, NS = 2 (up to 10) 13.8 us, NS = 4 (up to 12) 15.9 us.
+static int choose_strips_per_wg(int64_t strips, int cus) {
+    if (cus <= 0) cus = 1;
+    int best = 1;
+    int64_t best_load = INT64_MAX;
+    for (int ns = 1; ns <= kMaxStripsPerWg; ++ns) {
+        const int64_t wgs = (strips + ns - 1) / ns;
+        const int64_t load = (wgs + cus - 1) / cus * ns;
+        if (load <= best_load) {
+            best_load = load;
+            best = ns;
+        }
+    }
+    return best;
+}
+
 DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int cus) {
     DecodePlan p{};
     p.rows = choose_rows(M);
-    (void)cus;
-    p.strips_per_wg = kStripsPerWg;
+    p.strips = N / p.rows;
+    p.strips_per_wg = choose_strips_per_wg(p.strips, cus);
     if (const char* e = getenv("FP8BS_DECODE_STRIPS")) {    // tuning hook
         const int v = atoi(e);
-        if (v >= 1 && v <= 4) p.strips_per_wg = v;
+        if (v >= 1 && v <= kMaxStripsPerWg) p.strips_per_wg = v;
     }
-    p.strips = N / p.rows;
     p.workgroups = (p.strips + p.strips_per_wg - 1) / p.strips_per_wg;
     p.kblocks = K / kGroup;
     const int64_t super_blocks = (p.kblocks + (16 / p.rows) - 1) / (16 / p.rows);
@@ -190,16 +213,30 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int cus) {
         const int v = atoi(e);
         if (v >= 1 && v <= kDecodeMaxWaves) p.waves = v;
     }
+    // Two super blocks per load batch only when a CU holds at most one workgroup
+    // (then its waves alone keep the loads in flight) and a wave has more than one
+    // super block.  With more workgroups per CU the smaller batch (fewer registers,
+    // more waves resident) was faster (M = 8, N = 16384, K = 7168, NS = 4: 23.6 us
+    // against 25.7 us).
+    p.batch = p.workgroups <= cus && super_blocks > p.waves ? 2 : 1;
+    if (const char* e = getenv("FP8BS_DECODE_BATCH")) {     // tuning hook
+        const int v = atoi(e);
+        if (v >= 1 && v <= 2) p.batch = v;
+    }
     return p;
 }
 
 template <int P>
 static void launch_p(const DecodePlan& plan, dim3 grid, dim3 block, unsigned lds, hipStream_t st, const DecodeArgs& a) {
-    switch (plan.strips_per_wg) {
-        case 1: hipLaunchKernelGGL((gemm_decode_kernel<P, 1>), grid, block, lds, st, a); break;
-        case 2: hipLaunchKernelGGL((gemm_decode_kernel<P, 2>), grid, block, lds, st, a); break;
-        case 3: hipLaunchKernelGGL((gemm_decode_kernel<P, 3>), grid, block, lds, st, a); break;
-        default: hipLaunchKernelGGL((gemm_decode_kernel<P, 4>), grid, block, lds, st, a); break;
+    switch (plan.strips_per_wg * 10 + plan.batch) {
+        case 11: hipLaunchKernelGGL((gemm_decode_kernel<P, 1, 1>), grid, block, lds, st, a); break;
+        case 12: hipLaunchKernelGGL((gemm_decode_kernel<P, 1, 2>), grid, block, lds, st, a); break;
+        case 21: hipLaunchKernelGGL((gemm_decode_kernel<P, 2, 1>), grid, block, lds, st, a); break;
+        case 22: hipLaunchKernelGGL((gemm_decode_kernel<P, 2, 2>), grid, block, lds, st, a); break;
+        case 31: hipLaunchKernelGGL((gemm_decode_kernel<P, 3, 1>), grid, block, lds, st, a); break;
+        case 32: hipLaunchKernelGGL((gemm_decode_kernel<P, 3, 2>), grid, block, lds, st, a); break;
+        case 41: hipLaunchKernelGGL((gemm_decode_kernel<P, 4, 1>), grid, block, lds, st, a); break;
+        default: hipLaunchKernelGGL((gemm_decode_kernel<P, 4, 2>), grid, block, lds, st, a); break;
     }
 }
 

@@ -41,6 +41,7 @@ struct DecodePlan {
     int64_t workgroups;  // ceil(strips / strips_per_wg)
     int64_t kblocks;     // K / 128
     int waves;           // waves per workgroup = K splits
+    int batch;           // super blocks whose loads are issued together (1 or 2)
 };
 
 DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int cus);

@@ -140,13 +140,17 @@ def test_decode_activations_beyond_lds(M, K):
     check_linear(x, w, "decode, activations from global")
 
 
+@pytest.mark.parametrize("batch", [1, 2])
 @pytest.mark.parametrize("strips", [1, 2, 3, 4])
 @pytest.mark.parametrize("M,N", [(1, 640), (5, 384), (8, 1152), (12, 640)])
-def test_decode_strips_per_workgroup(strips, M, N, monkeypatch):
-    """Every strips-per-workgroup setting, including a partial last workgroup."""
+def test_decode_strips_per_workgroup(strips, batch, M, N, monkeypatch):
+    """Every strips-per-workgroup setting and load batch (super blocks whose loads
+    are issued together), including a partial last workgroup, a partial last
+    super block (K = 1408: 11 K blocks) and a partial last batch."""
     monkeypatch.setenv("FP8BS_DECODE_STRIPS", str(strips))
+    monkeypatch.setenv("FP8BS_DECODE_BATCH", str(batch))
     x, w = inputs(M, N, 1408, seed=80 + strips + M)
-    check_linear(x, w, f"decode strips={strips}")
+    check_linear(x, w, f"decode strips={strips} batch={batch}")
 
 
 @pytest.mark.parametrize("waves", [1, 2, 3, 5, 7, 16])
