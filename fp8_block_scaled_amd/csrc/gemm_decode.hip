@@ -45,7 +45,11 @@
 
 namespace fp8bs {
 
-constexpr int kDecodeMaxWaves = 16;
+// At most 8 waves per workgroup: the launch bound then allows 128+ VGPRs per wave,
+// so 4 strips with two super blocks per batch (136 VGPRs) do not spill.  A bound of
+// 16 waves capped them at 128 and spilled; the 8-wave bound measured 2.5% faster at
+// M = 8, N = 16384, K = 7168 and equal elsewhere.
+constexpr int kDecodeMaxWaves = 8;
 // Workgroup shape, from measurement on the decode shapes (M = 1 and 8, K = 7168
 // and 8192, N = 7168..16384): 8 waves per workgroup; fewer leave a CU short of
 // loads in flight.  Strips per workgroup (1..4) are chosen per shape in

@@ -153,7 +153,7 @@ def test_decode_strips_per_workgroup(strips, batch, M, N, monkeypatch):
     check_linear(x, w, f"decode strips={strips} batch={batch}")
 
 
-@pytest.mark.parametrize("waves", [1, 2, 3, 5, 7, 16])
+@pytest.mark.parametrize("waves", [1, 2, 3, 5, 7, 8])
 def test_decode_split_counts(waves, monkeypatch):
     """Every split-K degree of the decode schedule meets the tolerance."""
     monkeypatch.setenv("FP8BS_DECODE_WAVES", str(waves))
