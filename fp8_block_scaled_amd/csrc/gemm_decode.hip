@@ -179,32 +179,14 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
 // Row-group size for M tokens: the smallest of 4, 8, 16 that holds them.
 static int choose_rows(int64_t M) { return M <= 4 ? 4 : (M <= 8 ? 8 : 16); }
 
-// Strips per workgroup.  The workgroups are spread round-robin over the CUs and a
-// CU's own bandwidth is limited, so the time follows the most strips any CU
-// receives: ceil(workgroups / cus) * NS.  Take the NS that makes it smallest, and
-// of equals the largest (fewer workgroups, fewer re-reads of the activations).
-// Measured at M = 1, N = 9216, K = 7168 (2304 strips of 4): NS = 3 (9 strips on
-// every CU) 13.4 us, NS = 2 (up to 10) 13.8 us, NS = 4 (up to 12) 15.9 us.
-static int choose_strips_per_wg(int64_t strips, int cus) {
-    if (cus <= 0) cus = 1;
-    int best = 1;
-    int64_t best_load = INT64_MAX;
-    for (int ns = 1; ns <= kMaxStripsPerWg; ++ns) {
-        const int64_t wgs = (strips + ns - 1) / ns;
-        const int64_t load = (wgs + cus - 1) / cus * ns;
-        if (load <= best_load) {
-            best_load = load;
-            best = ns;
-        }
-    }
-    return best;
-}
-
 DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int cus) {
     DecodePlan p{};
     p.rows = choose_rows(M);
     p.strips = N / p.rows;
-    p.strips_per_wg = choose_strips_per_wg(p.strips, cus);
+    // Measured at M = 1, N = 9216, K = 7168 (2304 strips of 4): NS = 3 (9 strips on
+    // every CU) 13.4 us, NS = 2 (up to 10) 13.8 us, NS = 4 (up to 12) 15.9 us; at
+    // M = 8, N = 16384 NS = 1, 2, 3, 4 took 36.3, 25.5, 26.7, 23.6 us.
+    p.strips_per_wg = decode_strips_per_wg(p.strips, cus, p.rows * K, M * K, kMaxStripsPerWg);
     if (const char* e = getenv("FP8BS_DECODE_STRIPS")) {    // tuning hook
         const int v = atoi(e);
         if (v >= 1 && v <= kMaxStripsPerWg) p.strips_per_wg = v;
@@ -217,12 +199,13 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int cus) {
         const int v = atoi(e);
         if (v >= 1 && v <= kDecodeMaxWaves) p.waves = v;
     }
-    // Two super blocks per load batch only when a CU holds at most one workgroup
-    // (then its waves alone keep the loads in flight) and a wave has more than one
-    // super block.  With more workgroups per CU the smaller batch (fewer registers,
-    // more waves resident) was faster (M = 8, N = 16384, K = 7168, NS = 4: 23.6 us
-    // against 25.7 us).
-    p.batch = p.workgroups <= cus && super_blocks > p.waves ? 2 : 1;
+    // Two super blocks per load batch when a wave has more than one and a CU holds
+    // fewer than two workgroups on average: with 16 waves or more per CU one super
+    // block per wave keeps enough loads in flight, and the deeper batch only costs
+    // registers (M = 8, N = 16384, K = 7168, NS = 4, 2 workgroups per CU: 25.6 us
+    // with two against 23.0 us); with fewer waves it makes up for them (M = 8,
+    // N = 7168, K = 8192, 0.875 per CU: 15.2 against 16.0 us).
+    p.batch = super_blocks > p.waves && p.workgroups < 2 * (int64_t)cus ? 2 : 1;
     if (const char* e = getenv("FP8BS_DECODE_BATCH")) {     // tuning hook
         const int v = atoi(e);
         if (v >= 1 && v <= 2) p.batch = v;

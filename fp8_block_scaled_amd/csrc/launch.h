@@ -34,6 +34,27 @@ hipError_t launch_quant_weight(const void* w, void* qw, float* ws, int64_t N, in
 // ---- decode GEMM (M <= kDecodeMaxM): one workgroup per strip of `rows` columns, split-K over its waves
 constexpr int kDecodeMaxM = 16;
 
+// Strips per workgroup for the weight-streaming decode kernels.  Workgroups go
+// round-robin to the CUs and a CU's own bandwidth is limited, so the time follows
+// what the busiest CU moves: ceil(workgroups / cus) workgroups, each NS strips of
+// weights (`strip_bytes` each, from HBM) and one copy of the activations
+// (`act_bytes`, from L2, counted at half weight).  Returns the NS in 1..max_ns that
+// makes it smallest and, of equals, the largest (fewer workgroups).
+inline int decode_strips_per_wg(int64_t strips, int cus, int64_t strip_bytes, int64_t act_bytes, int max_ns) {
+    if (cus <= 0) cus = 1;
+    int best = 1;
+    double best_cost = 0.0;
+    for (int ns = 1; ns <= max_ns; ++ns) {
+        const int64_t wgs = (strips + ns - 1) / ns;
+        const double cost = (double)((wgs + cus - 1) / cus) * ((double)ns * strip_bytes + 0.5 * act_bytes);
+        if (ns == 1 || cost <= best_cost) {
+            best_cost = cost;
+            best = ns;
+        }
+    }
+    return best;
+}
+
 struct DecodePlan {
     int rows;            // 4, 8 or 16: token rows per MFMA group = output columns per strip
     int strips_per_wg;   // 1..4 adjacent strips per workgroup
@@ -95,7 +116,7 @@ struct W4Plan {
     int64_t kblocks;     // K / 128
     int waves;           // waves per workgroup = K splits
     int decode_p;        // > 0: decode kernel (M <= 16) with strips of P columns
-    int decode_ns;       //   strips per workgroup (1, 2 or 4)
+    int decode_ns;       //   strips per workgroup (1..4)
     int decode_ch;       //   super blocks per load batch (1 or 2)
     int64_t decode_wgs;
     int tile;            // > 0: LDS-tiled kernel, BM * 1000 + BN

@@ -221,8 +221,10 @@ __global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_stream_kernel(W4Args a
 // already inside the dequantized operand, so no promotion step is needed.
 //
 // One workgroup owns NS adjacent strips; its S waves take equal contiguous ranges
-// of super blocks and each requests the fragments of CH super blocks at a time
-// (branch-free: chunks past K are clamped to valid addresses and zeroed at use).
+// of super blocks and each requests the fragments of CH super blocks before it uses
+// any.  Branch-free, so that no load is sunk past another super block's MFMAs: a
+// super block past the wave's range re-reads the wave's last one, chunks past K are
+// clamped to the last one, and both are zeroed at use.
 // The waves are light on registers, so a CU holds several workgroups and many
 // loads in flight.  Partial sums over waves and groups are added through LDS in a
 // fixed order (deterministic).
@@ -258,7 +260,8 @@ __global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_decode_kernel(W4Args a
     auto load_batch = [&](int64_t sb) {
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            int64_t kc = (sb + i) * G + t;                       // K block of this lane's chunk
+            const int64_t sbi = sb + i < sb1 ? sb + i : sb1 - 1;
+            int64_t kc = sbi * G + t;                            // K block of this lane's chunk
             kc = kc < a.KB ? kc : a.KB - 1;
             const v4i* xp = reinterpret_cast<const v4i*>(xrow + kc * kGroup);
 #pragma unroll
@@ -277,22 +280,21 @@ __global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_decode_kernel(W4Args a
     const v4i z4 = {0, 0, 0, 0};
     for (int64_t sb = sb0; sb < sb1; sb += CH) {
         load_batch(sb);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            if (sb + i < sb1) {                                  // uniform
-                const bool use = mvalid && (sb + i) * G + t < a.KB;
-                v8bf xa[4];
+            const bool use = mvalid && sb + i < sb1 && (sb + i) * G + t < a.KB;
+            v8bf xa[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) xa[u] = as_bf8(use ? xv[i][u] : z4);
+            for (int u = 0; u < 4; ++u) xa[u] = as_bf8(use ? xv[i][u] : z4);
 #pragma unroll
-                for (int q = 0; q < NS; ++q) {
-                    const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sv[i][q], 0);
-                    const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)sv[i][q], 1);
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0], dequant8((uint32_t)wv[i][q].x, s0), acc[q], 0, 0, 0);
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[1], dequant8((uint32_t)wv[i][q].y, s0), acc[q], 0, 0, 0);
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[2], dequant8((uint32_t)wv[i][q].z, s1), acc[q], 0, 0, 0);
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[3], dequant8((uint32_t)wv[i][q].w, s1), acc[q], 0, 0, 0);
-                }
+            for (int q = 0; q < NS; ++q) {
+                const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sv[i][q], 0);
+                const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)sv[i][q], 1);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0], dequant8((uint32_t)wv[i][q].x, s0), acc[q], 0, 0, 0);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[1], dequant8((uint32_t)wv[i][q].y, s0), acc[q], 0, 0, 0);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[2], dequant8((uint32_t)wv[i][q].z, s1), acc[q], 0, 0, 0);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[3], dequant8((uint32_t)wv[i][q].w, s1), acc[q], 0, 0, 0);
             }
         }
     }
@@ -628,17 +630,12 @@ W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus, size_t workspace_byt
         const int P = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
         p.decode_p = P;
         const int64_t strips = N / P;
-        // Four strips per workgroup once there are 12 per CU (gate/up: 4096 strips on
-        // 256 CUs); fewer (q/k/v: 2304) run faster with two (measured).
-        p.decode_ns = strips >= 12 * (int64_t)cus ? 4 : 2;
+        // A strip is P rows of codes and scales (K / 2 + K / 16 bytes each); every
+        // workgroup also reads the M x K BF16 activations.
+        p.decode_ns = decode_strips_per_wg(strips, cus, P * (K / 2 + K / 16), 2 * M * K, 4);
         if (const char* e = getenv("FP8BS_W4_DECODE_NS")) {   // tuning hook
             const int v = atoi(e);
-            if (v == 1 || v == 2 || v == 4) p.decode_ns = v;
-        }
-        p.decode_ch = p.decode_ns <= 2 ? 2 : 1;
-        if (const char* e = getenv("FP8BS_W4_DECODE_CH")) {   // tuning hook
-            const int v = atoi(e);
-            if (v == 1 || v == 2) p.decode_ch = v;
+            if (v >= 1 && v <= 4) p.decode_ns = v;
         }
         const int64_t SB = (p.kblocks + 16 / P - 1) / (16 / P);
         p.waves = (int)(SB < kW4MaxWaves ? SB : kW4MaxWaves);
@@ -647,6 +644,15 @@ W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus, size_t workspace_byt
             if (v >= 1 && v <= kW4MaxWaves && v <= SB) p.waves = v;
         }
         p.decode_wgs = (strips + p.decode_ns - 1) / p.decode_ns;
+        // Two super blocks per load batch when a wave has more than one and a CU
+        // holds fewer than two workgroups on average, as in the FP8 decode kernel
+        // (M = 1, N = 7168, K = 8192, 448 workgroups: 10.3 us against 11.4 us with one
+        // super block; q/k/v, 768 workgroups: 11.9 against 12.3 us).
+        p.decode_ch = SB > p.waves && p.decode_wgs < 2 * (int64_t)cus ? 2 : 1;
+        if (const char* e = getenv("FP8BS_W4_DECODE_CH")) {   // tuning hook
+            const int v = atoi(e);
+            if (v == 1 || v == 2) p.decode_ch = v;
+        }
     }
     return p;
 }
@@ -659,12 +665,19 @@ static hipError_t launch_w4_decode(const W4Plan& plan, hipStream_t st, const W4A
     return hipGetLastError();
 }
 
+template <int P, int NS>
+static hipError_t launch_w4_decode_ns(const W4Plan& plan, hipStream_t st, const W4Args& a) {
+    return plan.decode_ch == 2 ? launch_w4_decode<P, NS, 2>(plan, st, a) : launch_w4_decode<P, NS, 1>(plan, st, a);
+}
+
 template <int P>
 static hipError_t launch_w4_decode_p(const W4Plan& plan, hipStream_t st, const W4Args& a) {
-    if (plan.decode_ns == 4) return launch_w4_decode<P, 4, 1>(plan, st, a);
-    if (plan.decode_ns == 2)
-        return plan.decode_ch == 2 ? launch_w4_decode<P, 2, 2>(plan, st, a) : launch_w4_decode<P, 2, 1>(plan, st, a);
-    return plan.decode_ch == 2 ? launch_w4_decode<P, 1, 2>(plan, st, a) : launch_w4_decode<P, 1, 1>(plan, st, a);
+    switch (plan.decode_ns) {
+        case 1: return launch_w4_decode_ns<P, 1>(plan, st, a);
+        case 2: return launch_w4_decode_ns<P, 2>(plan, st, a);
+        case 3: return launch_w4_decode_ns<P, 3>(plan, st, a);
+        default: return launch_w4_decode_ns<P, 4>(plan, st, a);
+    }
 }
 
 template <int R, int NS>

@@ -119,6 +119,15 @@ DECODE_CASES = [
     (3, 1024, 1024, {"FP8BS_W4_DECODE_NS": "1", "FP8BS_W4_DECODE_CH": "2"}),
     (16, 512, 1024, {"FP8BS_W4_DECODE_WAVES": "3"}), (1, 896, 384, {"FP8BS_W4_DECODE_WAVES": "2"}),
     (4, 7168, 1024, {"FP8BS_W4_DECODE_WAVES": "5", "FP8BS_W4_DECODE_CH": "2"}),
+    # every strip count with both batch sizes, partial last workgroups (40 strips of 16 in 3s)
+    (1, 7168, 2048, {"FP8BS_W4_DECODE_NS": "3", "FP8BS_W4_DECODE_CH": "1"}),
+    (1, 7168, 2048, {"FP8BS_W4_DECODE_NS": "3", "FP8BS_W4_DECODE_CH": "2"}),
+    (6, 4096, 1152, {"FP8BS_W4_DECODE_NS": "3", "FP8BS_W4_DECODE_CH": "2"}),
+    (12, 1024, 640, {"FP8BS_W4_DECODE_NS": "3"}),
+    (2, 2048, 1152, {"FP8BS_W4_DECODE_NS": "4", "FP8BS_W4_DECODE_CH": "2"}),
+    (9, 8576, 1024, {"FP8BS_W4_DECODE_NS": "4", "FP8BS_W4_DECODE_CH": "2"}),
+    (16, 2048, 384, {"FP8BS_W4_DECODE_NS": "2", "FP8BS_W4_DECODE_CH": "2"}),
+    (5, 1152, 384, {"FP8BS_W4_DECODE_NS": "2", "FP8BS_W4_DECODE_CH": "1"}),
 ]
 
 
