@@ -9,9 +9,13 @@
 // 128-wide scale block at a time through two LDS stages:
 //   1. at the top of step kb the wave waits for its own copies into stage kb%2
 //      and the workgroup meets at a barrier; the copies of K block kb + 1 into the
-//      other stage are then issued, two per subtile row over the first rows --
-//      direct global -> LDS loads (global_load_lds_dwordx4: no VGPRs, no LDS write
-//      instructions), overlapping the compute of step kb.  With 128 x 256 tiles each
+//      other stage are then issued over the first subtile rows -- direct global ->
+//      LDS loads (global_load_lds_dwordx4: no VGPRs, no LDS write instructions),
+//      overlapping the compute of step kb.  A copy that the memory pipeline cannot
+//      take yet stalls its wave, MFMAs included, so with 256 x 256 tiles waves 0-3
+//      (one per SIMD) issue all of them, 8 per subtile row over the first two rows,
+//      while the other wave on each SIMD keeps the MFMA pipe busy; the smaller
+//      tiles spread them over every wave, two per row.  With 128 x 256 tiles each
 //      thread also touches one 128-byte line of K block kb + 2 (a 4-byte
 //      direct-to-LDS load into a dump area) so that the next copies find their
 //      lines in L2; measured with this schedule, the touch pays for that shape
@@ -65,6 +69,14 @@ struct PrefillArgs {
 constexpr int stage_bytes(int BM, int BN) { return (BM + BN) * 128 + BM * 4 + 256; }
 // Tile shapes whose K loop touches the lines of K block kb + 2 ahead of the copies.
 constexpr bool prefill_warm(int BM, int BN) { return BM == 128 && BN == 256; }
+// Waves that issue the stage copies, and copies per subtile row.  256 x 256 tiles: 4
+// waves (one per SIMD), 8 per row -- measured against all 8 waves with 2 per row:
+// prefill_oproj 424 -> 412 us, fusion_fc 4.74 -> 4.52 ms, M = 2048 on the 7168 x 7168
+// projection 131.5 -> 125.4 us (4 per row: 418 us / 4.58 ms; 16 in the first row:
+// 431 us / 4.71 ms).  The smaller tiles were slower that way (M = 64, split-K 128 x 128
+// tiles: 25.7 -> 29.8 us), so they keep every wave, 2 per row.
+constexpr int prefill_copy_waves(int BM, int BN, int waves) { return BM == 256 && BN == 256 ? 4 : waves; }
+constexpr int prefill_copies_per_row(int BM, int BN) { return BM == 256 && BN == 256 ? 8 : 2; }
 // Dynamic LDS of a launch: two stages, plus the 256-byte dump of the warm-up touches.
 constexpr int prefill_lds_bytes(int BM, int BN) { return 2 * stage_bytes(BM, BN) + (prefill_warm(BM, BN) ? 256 : 0); }
 
@@ -91,15 +103,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
     constexpr int TJ = WTM / 16, TI = WTN / 16;         // subtiles (m, n)
     constexpr int kStage = stage_bytes(BM, BN);
     // A stage is (BM + BN) / 8 copy units of 8 tile rows (1 KiB, one 64-lane
-    // 16-byte direct-to-LDS load); wave w takes kUnitsLo or kUnitsLo + 1 of them.
+    // 16-byte direct-to-LDS load); copying wave w takes kUnitsLo or kUnitsLo + 1 of
+    // them.
     constexpr int kUnits = (BM + BN) / 8;
-    constexpr int kUnitsLo = kUnits / kWaves, kUnitsExtra = kUnits % kWaves;
-    constexpr int kCopies = kUnitsLo + (kUnitsExtra ? 1 : 0);    // per wave, at most
-    constexpr int kCopyRows = (kCopies + 1) / 2;                  // subtile rows issuing copies
+    constexpr int kCopyWaves = prefill_copy_waves(BM, BN, kWaves);
+    constexpr int kUnitsLo = kUnits / kCopyWaves, kUnitsExtra = kUnits % kCopyWaves;
+    constexpr int kCopies = kUnitsLo + (kUnitsExtra ? 1 : 0);    // per copying wave, at most
+    constexpr int kPer = prefill_copies_per_row(BM, BN);          // copies per subtile row
+    constexpr int kCopyRows = (kCopies + kPer - 1) / kPer;        // subtile rows issuing copies
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tiles are whole MFMA subtiles");
     static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's n-range must lie in one weight block");
     static_assert(BN % 8 == 0 && BM % 8 == 0, "copies: 8-row groups");
-    static_assert(kCopyRows <= TI, "two copies per subtile row");
+    static_assert(kCopyRows <= TI, "the copies fit the subtile rows");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     // ---- tile selection: XCD-contiguous, grouped raster
@@ -140,8 +155,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
     // through its parity (the swizzle): two offsets serve all copies -- except
     // with CLAMP, where rows past M are replaced by row M - 1 and the offset is
     // formed per copy.
-    const int ucount = kUnitsLo + (wave < kUnitsExtra ? 1 : 0);
-    const int ubase = wave * kUnitsLo + (wave < kUnitsExtra ? wave : kUnitsExtra);
+    const int ucount = wave < kCopyWaves ? kUnitsLo + (wave < kUnitsExtra ? 1 : 0) : 0;
+    const int ubase = wave < kCopyWaves ? wave * kUnitsLo + (wave < kUnitsExtra ? wave : kUnitsExtra) : 0;
     const int lrow = lane >> 3;
     uint32_t voff[2];
 #pragma unroll
@@ -309,8 +324,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
             // into the idle stage (no branch in the loop).
             const int64_t kn = more ? kb + 1 : kb;
             if (i < kCopyRows) {
-                copy_one(kn, stage ^ 1, 2 * i);
-                if (2 * i + 1 < kCopies) copy_one(kn, stage ^ 1, 2 * i + 1);
+#pragma unroll
+                for (int c = 0; c < kPer; ++c)
+                    if (kPer * i + c < kCopies) copy_one(kn, stage ^ 1, kPer * i + c);
             }
             if (i == kCopyRows - 1) {
                 copy_scales(kn, stage ^ 1);
