@@ -28,7 +28,9 @@
 //     activation traffic against the number of workgroups; it is chosen per shape
 //     so that every CU receives as nearly the same number of strips as possible.
 //   * Each lane requests the fragments and scales of CH super blocks at a time.
-//     The weight scale index is made wave-uniform.
+//     The weight scale index is made wave-uniform.  Weight loads read whole cache
+//     lines (a DPP exchange between partner lanes restores the operand layout) and
+//     are nontemporal.
 //
 // Operand layout per lane l (g = l / 16, r = l % 16, row rr = r % P, group
 // tb = r / P): A row r = weight row n0 + rr at K block kbase + tb; B column r =
@@ -84,14 +86,35 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
     const int64_t sb1 = ((wave + 1) * SKB) / S;
     const uint8_t* xrow = a.x + (mvalid ? rr : 0) * a.K + 16 * g;
     const float* xsrow = a.xs + (mvalid ? rr : 0) * a.KB;
-    const uint8_t* wrow[NS];
+    // Weight loads read whole 128-byte lines.  Lanes r and r ^ 8 of a 16-lane row
+    // are partners (operand rows pair(r) and pair(r ^ 8), pair p = weight row p % P
+    // at K block p / P of the super block): the first load of lane r takes chunk
+    // c = g + 4 hh (hh = r / 8) of pair r ^ 8 hh, the second chunk c of the other
+    // pair, so each load instruction covers 8 lines in full (chunks 0-3 from one
+    // partner, 4-7 from the other) instead of 16 halves.  One DPP exchange between
+    // partners then leaves every lane with chunks g and g + 4 of its own pair, the
+    // layout described above.  With each line requested once, the weight loads are
+    // nontemporal: the stream, read once, does not displace the activations and other
+    // data in the caches.  (Half-line loads, each line requested by two instructions,
+    // lost with nontemporal loads: the second request missed.)  Measured together in
+    // one session against half-line temporal loads: M = 1, N = 9216, K = 7168 13.4 ->
+    // 12.2 us; M = 8, N = 16384, K = 7168 23.0 -> 21.8 us; M = 8, N = 7168, K = 8192
+    // 15.2 -> 14.6 us; whole lines with temporal loads were 0.1-0.5 us slower than
+    // half lines.
+    const int hh = r >> 3;
+    const int pA = r ^ (8 * hh), pB = pA ^ 8;
+    const int rowA = pA % P, tbA = pA / P, rowB = pB % P, tbB = pB / P;
+    const int cw = 16 * (g + 4 * hh);
+    const uint8_t* wrowA[NS];
+    const uint8_t* wrowB[NS];
     const float* wsrow[NS];
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
         // Strips past the last one (a partial final workgroup) re-read the last
         // strip; their results are not stored.
         const int64_t st = strip0 + q < a.strips ? strip0 + q : a.strips - 1;
-        wrow[q] = a.w + (st * P + rr) * a.K + 16 * g;
+        wrowA[q] = a.w + (st * P + rowA) * a.K + cw;
+        wrowB[q] = a.w + (st * P + rowB) * a.K + cw;
         wsrow[q] = a.ws + ((st * P) / kGroup) * a.KB;
     }
 
@@ -106,17 +129,18 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int64_t sbi = sb + i < sb1 ? sb + i : sb1 - 1;
-            int64_t k = sbi * G + tb;
+            int64_t k = sbi * G + tb, kA = sbi * G + tbA, kB = sbi * G + tbB;
             k = k < a.KB ? k : a.KB - 1;
+            kA = kA < a.KB ? kA : a.KB - 1;
+            kB = kB < a.KB ? kB : a.KB - 1;
             const v4i* xp = reinterpret_cast<const v4i*>(xrow + k * kGroup);
             xv[i][0] = xp[0];
             xv[i][1] = xp[4];
             xsv[i] = xsrow[k];
 #pragma unroll
             for (int q = 0; q < NS; ++q) {
-                const v4i* wp = reinterpret_cast<const v4i*>(wrow[q] + k * kGroup);
-                wv[i][q][0] = wp[0];
-                wv[i][q][1] = wp[4];
+                wv[i][q][0] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrowA[q] + kA * kGroup));
+                wv[i][q][1] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrowB[q] + kB * kGroup));
                 wsv[i][q] = wsrow[q][k];
             }
         }
@@ -138,8 +162,17 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
             const float xsc = use ? xsv[i] : 0.0f;
 #pragma unroll
             for (int q = 0; q < NS; ++q) {
-                const v8i av = {wv[i][q][0].x, wv[i][q][0].y, wv[i][q][0].z, wv[i][q][0].w,
-                                wv[i][q][1].x, wv[i][q][1].y, wv[i][q][1].z, wv[i][q][1].w};
+                // The partner exchange: send the chunk that belongs to the partner, keep
+                // the own one (DPP row_ror:8 swaps lanes r and r ^ 8 of each row).
+                const v4i la = wv[i][q][0], lb = wv[i][q][1];
+                const v4i snd = hh ? la : lb;
+                v4i rcv;
+                rcv.x = __builtin_amdgcn_update_dpp(0, snd.x, 0x128, 0xF, 0xF, false);
+                rcv.y = __builtin_amdgcn_update_dpp(0, snd.y, 0x128, 0xF, 0xF, false);
+                rcv.z = __builtin_amdgcn_update_dpp(0, snd.z, 0x128, 0xF, 0xF, false);
+                rcv.w = __builtin_amdgcn_update_dpp(0, snd.w, 0x128, 0xF, 0xF, false);
+                const v4i lo = hh ? rcv : la, hi = hh ? lb : rcv;      // chunks g and g + 4
+                const v8i av = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
                 // Format 0 = E4M3 for both operands; zero scale operands select the unscaled MFMA.
                 const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, zero, 0, 0, 0, 0, 0, 0);
                 const float sc = xsc * wsv[i][q];
@@ -199,13 +232,11 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int cus) {
         const int v = atoi(e);
         if (v >= 1 && v <= kDecodeMaxWaves) p.waves = v;
     }
-    // Two super blocks per load batch when a wave has more than one and a CU holds
-    // fewer than two workgroups on average: with 16 waves or more per CU one super
-    // block per wave keeps enough loads in flight, and the deeper batch only costs
-    // registers (M = 8, N = 16384, K = 7168, NS = 4, 2 workgroups per CU: 25.6 us
-    // with two against 23.0 us); with fewer waves it makes up for them (M = 8,
-    // N = 7168, K = 8192, 0.875 per CU: 15.2 against 16.0 us).
-    p.batch = super_blocks > p.waves && p.workgroups < 2 * (int64_t)cus ? 2 : 1;
+    // One super block per load batch: with whole-line nontemporal weight loads the
+    // batch of two was slower on every decode shape measured (M = 8, N = 7168,
+    // K = 8192, NS = 4: 14.4 against 13.9 us; M = 1, N = 9216, K = 7168, NS = 3: 13.0
+    // against 12.2 us).  Batches of two stay reachable through the tuning hook.
+    p.batch = 1;
     if (const char* e = getenv("FP8BS_DECODE_BATCH")) {     // tuning hook
         const int v = atoi(e);
         if (v >= 1 && v <= 2) p.batch = v;

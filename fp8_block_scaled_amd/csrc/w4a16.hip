@@ -268,7 +268,9 @@ __global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_decode_kernel(W4Args a
             for (int u = 0; u < 4; ++u) xv[i][u] = xp[u];
 #pragma unroll
             for (int q = 0; q < NS; ++q) {
-                wv[i][q] = *reinterpret_cast<const v4i*>(wrow[q] + kc * 64);
+                // Nontemporal: the code stream is read once; at P = 4 and 8 one load
+                // instruction covers whole 128-byte lines (G adjacent K blocks of a row).
+                wv[i][q] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow[q] + kc * 64));
                 sv[i][q] = *reinterpret_cast<const uint16_t*>(srow[q] + kc * 8);
             }
         }
