@@ -61,14 +61,24 @@ __global__ __launch_bounds__(kMidMaxWaves * 64) void gemm_mid_kernel(MidArgs a) 
         xrow[rho] = a.x + (int64_t)m * a.K + 16 * g;
         xsrow[rho] = a.xs + (int64_t)m * a.KB;
     }
-    const uint8_t* wrow[NS];
+    // Weight loads read whole 128-byte lines, as in the decode kernel: lanes r and
+    // r ^ 8 are partners; the first load of lane r takes chunk c = g + 4 hh (hh = r / 8)
+    // of strip row r ^ 8 hh, the second chunk c of the other partner's row, and a DPP
+    // exchange leaves chunks g and g + 4 of row r in every lane.  The loads are
+    // nontemporal (the weight stream is read once).
+    const int hh = r >> 3;
+    const int rowA = r ^ (8 * hh), rowB = rowA ^ 8;
+    const int cw = 16 * (g + 4 * hh);
+    const uint8_t* wrowA[NS];
+    const uint8_t* wrowB[NS];
     const float* wsrow[NS];
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
         // Strips past the last one (a partial final workgroup) re-read the last
         // strip; their results are not stored.
         const int64_t st = strip0 + q < a.strips ? strip0 + q : a.strips - 1;
-        wrow[q] = a.w + (st * 16 + r) * a.K + 16 * g;
+        wrowA[q] = a.w + (st * 16 + rowA) * a.K + cw;
+        wrowB[q] = a.w + (st * 16 + rowB) * a.K + cw;
         wsrow[q] = a.ws + ((st * 16) / kGroup) * a.KB;
     }
 
@@ -87,9 +97,8 @@ __global__ __launch_bounds__(kMidMaxWaves * 64) void gemm_mid_kernel(MidArgs a) 
     auto load = [&](Frag& f, int64_t kb) {
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
-            const v4i* wp = reinterpret_cast<const v4i*>(wrow[q] + kb * kGroup);
-            f.wv[q][0] = wp[0];
-            f.wv[q][1] = wp[4];
+            f.wv[q][0] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrowA[q] + kb * kGroup));
+            f.wv[q][1] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrowB[q] + kb * kGroup));
             f.wsv[q] = wsrow[q][kb];
         }
 #pragma unroll
@@ -103,8 +112,16 @@ __global__ __launch_bounds__(kMidMaxWaves * 64) void gemm_mid_kernel(MidArgs a) 
     auto compute = [&](const Frag& f) {
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
-            const v8i av = {f.wv[q][0].x, f.wv[q][0].y, f.wv[q][0].z, f.wv[q][0].w,
-                            f.wv[q][1].x, f.wv[q][1].y, f.wv[q][1].z, f.wv[q][1].w};
+            // The partner exchange (DPP row_ror:8 swaps lanes r and r ^ 8 of each row).
+            const v4i la = f.wv[q][0], lb = f.wv[q][1];
+            const v4i snd = hh ? la : lb;
+            v4i rcv;
+            rcv.x = __builtin_amdgcn_update_dpp(0, snd.x, 0x128, 0xF, 0xF, false);
+            rcv.y = __builtin_amdgcn_update_dpp(0, snd.y, 0x128, 0xF, 0xF, false);
+            rcv.z = __builtin_amdgcn_update_dpp(0, snd.z, 0x128, 0xF, 0xF, false);
+            rcv.w = __builtin_amdgcn_update_dpp(0, snd.w, 0x128, 0xF, 0xF, false);
+            const v4i lo = hh ? rcv : la, hi = hh ? lb : rcv;          // chunks g and g + 4
+            const v8i av = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
             for (int rho = 0; rho < R; ++rho) {
                 const v8i bv = {f.xv[rho][0].x, f.xv[rho][0].y, f.xv[rho][0].z, f.xv[rho][0].w,
