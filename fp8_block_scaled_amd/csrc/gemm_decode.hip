@@ -47,6 +47,9 @@
 
 namespace fp8bs {
 
+typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef float f32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+
 // At most 8 waves per workgroup: the launch bound then allows 128+ VGPRs per wave,
 // so 4 strips with two super blocks per batch (136 VGPRs) do not spill.  A bound of
 // 16 waves capped them at 128 and spilled; the 8-wave bound measured 2.5% faster at
@@ -124,7 +127,13 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
     // past KB (a last, partial super block) is clamped to the last K block, and both
     // are zeroed at use.
     v4i wv[CH][NS][2], xv[CH][2];
-    float xsv[CH], wsv[CH][NS];
+    // Weight scales: the G K blocks of a super block have consecutive scales in a
+    // strip's scale row, at a wave-uniform address, so each strip's G scales come in
+    // one scalar load (from K block KB - G for a last, partial super block; the plan
+    // keeps KB >= G) and each lane picks its own, wsi.  The vector memory pipeline
+    // then carries only the fragments and the activation scales.
+    float xsv[CH], wsg[CH][NS][G];
+    int wsi[CH];
     auto load_batch = [&](int64_t sb) {
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
@@ -133,6 +142,8 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
             k = k < a.KB ? k : a.KB - 1;
             kA = kA < a.KB ? kA : a.KB - 1;
             kB = kB < a.KB ? kB : a.KB - 1;
+            const int64_t wbase = sbi * G + G <= a.KB ? sbi * G : a.KB - G;
+            wsi[i] = (int)(k - wbase);
             const v4i* xp = reinterpret_cast<const v4i*>(xrow + k * kGroup);
             xv[i][0] = xp[0];
             xv[i][1] = xp[4];
@@ -141,7 +152,19 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
             for (int q = 0; q < NS; ++q) {
                 wv[i][q][0] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrowA[q] + kA * kGroup));
                 wv[i][q][1] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrowB[q] + kB * kGroup));
-                wsv[i][q] = wsrow[q][k];
+                if constexpr (G == 4) {
+                    const f32x4_a4 v = *reinterpret_cast<const f32x4_a4*>(wsrow[q] + wbase);
+                    wsg[i][q][0] = v[0];
+                    wsg[i][q][1] = v[1];
+                    wsg[i][q][2] = v[2];
+                    wsg[i][q][3] = v[3];
+                } else if constexpr (G == 2) {
+                    const f32x2_a4 v = *reinterpret_cast<const f32x2_a4*>(wsrow[q] + wbase);
+                    wsg[i][q][0] = v[0];
+                    wsg[i][q][1] = v[1];
+                } else {
+                    wsg[i][q][0] = wsrow[q][wbase];
+                }
             }
         }
     };
@@ -175,7 +198,10 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
                 const v8i av = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
                 // Format 0 = E4M3 for both operands; zero scale operands select the unscaled MFMA.
                 const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, zero, 0, 0, 0, 0, 0, 0);
-                const float sc = xsc * wsv[i][q];
+                float wsl = wsg[i][q][0];
+#pragma unroll
+                for (int t = 1; t < G; ++t) wsl = wsi[i] == t ? wsg[i][q][t] : wsl;
+                const float sc = xsc * wsl;
                 acc[q][0] = fmaf(sc, p[0], acc[q][0]);
                 acc[q][1] = fmaf(sc, p[1], acc[q][1]);
                 acc[q][2] = fmaf(sc, p[2], acc[q][2]);
@@ -215,6 +241,7 @@ static int choose_rows(int64_t M) { return M <= 4 ? 4 : (M <= 8 ? 8 : 16); }
 DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int cus) {
     DecodePlan p{};
     p.rows = choose_rows(M);
+    while (16 / p.rows > K / kGroup) p.rows *= 2;          // KB >= G: a super block fits in K
     p.strips = N / p.rows;
     // Measured at M = 1, N = 9216, K = 7168 (2304 strips of 4): NS = 3 (9 strips on
     // every CU) 13.4 us, NS = 2 (up to 10) 13.8 us, NS = 4 (up to 12) 15.9 us; at
