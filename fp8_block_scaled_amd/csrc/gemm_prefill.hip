@@ -12,15 +12,16 @@
 //      other stage are then issued over the first subtile rows -- direct global ->
 //      LDS loads (global_load_lds_dwordx4: no VGPRs, no LDS write instructions),
 //      overlapping the compute of step kb.  A copy that the memory pipeline cannot
-//      take yet stalls its wave, MFMAs included, so with 256 x 256 tiles waves 0-3
-//      (one per SIMD) issue all of them, 8 per subtile row over the first two rows,
-//      while the other wave on each SIMD keeps the MFMA pipe busy; the smaller
-//      tiles spread them over every wave, two per row.  With 128 x 256 tiles each
-//      thread also touches one 128-byte line of K block kb + 2 (a 4-byte
-//      direct-to-LDS load into a dump area) so that the next copies find their
-//      lines in L2; measured with this schedule, the touch pays for that shape
-//      (M = 768 on the 7168 x 7168 projection: 85 against 93 us) and costs 2-8%
-//      on the others (its memory instructions outweigh the L2 misses they save);
+//      take yet stalls its wave, MFMAs included, so with BN = 256 tiles waves 0-3
+//      (one per SIMD) issue all of them, 8 per subtile row over the first two rows
+//      (128 x 256: 4 per row over three rows), while the other wave on each SIMD
+//      keeps the MFMA pipe busy; 128 x 128 tiles spread them over every wave, two
+//      per row.  With 128 x 256 tiles the copying waves also touch every line of
+//      K block kb + 2 (4-byte direct-to-LDS loads into a dump area) so that the
+//      next copies find their lines in L2; measured, the touch pays for that shape
+//      (M = 768 on the 7168 x 7168 projection: 85 against 93 us, before the copying
+//      waves) and costs 2-8% on the others (its memory instructions outweigh the L2
+//      misses they save);
 //   2. each wave runs v_mfma_f32_16x16x128_f8f6f4 over its 16 x 16 subtiles (A = 16
 //      weight rows, B = 16 token rows; one MFMA covers the whole K block) and folds
 //      each FP32 result into its accumulators with acc += (s[m] * ws[nb]) * P: the
@@ -73,10 +74,11 @@ constexpr bool prefill_warm(int BM, int BN) { return BM == 128 && BN == 256; }
 // waves (one per SIMD), 8 per row -- measured against all 8 waves with 2 per row:
 // prefill_oproj 424 -> 412 us, fusion_fc 4.74 -> 4.52 ms, M = 2048 on the 7168 x 7168
 // projection 131.5 -> 125.4 us (4 per row: 418 us / 4.58 ms; 16 in the first row:
-// 431 us / 4.71 ms).  The smaller tiles were slower that way (M = 64, split-K 128 x 128
-// tiles: 25.7 -> 29.8 us), so they keep every wave, 2 per row.
-constexpr int prefill_copy_waves(int BM, int BN, int waves) { return BM == 256 && BN == 256 ? 4 : waves; }
-constexpr int prefill_copies_per_row(int BM, int BN) { return BM == 256 && BN == 256 ? 8 : 2; }
+// 431 us / 4.71 ms).  128 x 256 tiles: 4 waves, 4 per row (M = 640 / 768 / 1024 on that
+// projection: 88.0 / 90.1 / 97.9 -> 82.8 / 84.4 / 92.8 us).  128 x 128 tiles were slower
+// that way (M = 64, split-K tiles: 25.7 -> 29.8 us), so they keep every wave, 2 per row.
+constexpr int prefill_copy_waves(int BM, int BN, int waves) { return BN == 256 ? 4 : waves; }
+constexpr int prefill_copies_per_row(int BM, int BN) { return BN == 256 ? (BM == 256 ? 8 : 4) : 2; }
 // Dynamic LDS of a launch: two stages, plus the 256-byte dump of the warm-up touches.
 constexpr int prefill_lds_bytes(int BM, int BN) { return 2 * stage_bytes(BM, BN) + (prefill_warm(BM, BN) ? 256 : 0); }
 
@@ -201,23 +203,35 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
         for (int c = 0; c < kCopies; ++c) copy_one(kb, stage, c);
     };
 
-    // ---- L2 warm-up of K block kb + 2 (WARM shapes): thread t touches stage row
-    // t mod (BM + BN) (one line), always as each wave's last vector load.
+    // ---- L2 warm-up of K block kb + 2 (WARM shapes): the copying waves touch every
+    // stage row, thread t rows t and t + 64 kCopyWaves (mod BM + BN), one line each,
+    // always as the wave's last two vector loads; the other waves issue none (a vector
+    // memory instruction on them costs their MFMAs: M = 640 / 768 / 1024 on the
+    // 7168 x 7168 projection, 83.4 / 85.0 / 92.6 us with one touch per thread of every
+    // wave, 78.6 / 81.1 / 90.8 us this way).
     constexpr bool WARM = prefill_warm(BM, BN);
-    static_assert(!WARM || BM + BN <= kThreads, "one warm-up line per thread covers the stage");
-    const int pf_row = tid % (BM + BN);
-    const bool pf_w = pf_row < BN;
-    int64_t pf_off;
+    static_assert(!WARM || BM + BN <= 2 * 64 * kCopyWaves, "two warm-up lines per copying thread cover the stage");
+    const int pf_row0 = tid % (BM + BN), pf_row1 = (tid + 64 * kCopyWaves) % (BM + BN);
+    const bool pf_w0 = pf_row0 < BN, pf_w1 = pf_row1 < BN;
+    int64_t pf_off0, pf_off1;
     {
-        int64_t row = pf_w ? n0 + pf_row : m0 + (pf_row - BN);
-        if (CLAMP && !pf_w) row = row < a.M ? row : a.M - 1;
-        pf_off = row * a.K;
+        int64_t row = pf_w0 ? n0 + pf_row0 : m0 + (pf_row0 - BN);
+        if (CLAMP && !pf_w0) row = row < a.M ? row : a.M - 1;
+        pf_off0 = row * a.K;
+        row = pf_w1 ? n0 + pf_row1 : m0 + (pf_row1 - BN);
+        if (CLAMP && !pf_w1) row = row < a.M ? row : a.M - 1;
+        pf_off1 = row * a.K;
     }
     auto warm = [&](int64_t kb) {
         if constexpr (WARM) {
-            const uint8_t* base = (pf_w ? a.w : a.x) + kb * kGroup;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + pf_off),
-                                             (__attribute__((address_space(3))) void*)(lds + 2 * kStage), 4, 0, 0);
+            if (wave < kCopyWaves) {                    // wave-uniform
+                const uint8_t* b0 = (pf_w0 ? a.w : a.x) + kb * kGroup;
+                const uint8_t* b1 = (pf_w1 ? a.w : a.x) + kb * kGroup;
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(b0 + pf_off0),
+                                                 (__attribute__((address_space(3))) void*)(lds + 2 * kStage), 4, 0, 0);
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(b1 + pf_off1),
+                                                 (__attribute__((address_space(3))) void*)(lds + 2 * kStage), 4, 0, 0);
+            }
         }
     };
 
@@ -282,13 +296,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
         af_next = lds_frag(wt, wn * WTN + r, g);
     };
     // This wave's copies into a stage (and the scale loads) have landed -- with the
-    // warm-up, all but the last load issued, the touch -- and it has consumed every
+    // warm-up, all but the last two loads issued, the touches -- and it has consumed every
     // LDS read of the other stage; the barrier makes everyone's copies visible.  A
     // plain s_barrier: __syncthreads() would add a full vmcnt(0) wait (its fence).  The
     // empty asm statements keep the compiler from moving LDS accesses across it.
     auto stage_ready = [&]() {
         if constexpr (WARM)
-            asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)" ::: "memory");
+            asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory");
         else
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
@@ -331,7 +345,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
             if (i == kCopyRows - 1) {
                 copy_scales(kn, stage ^ 1);
                 copy_wscales(kn, stage ^ 1);
-                warm(kb + 2 < kb1 ? kb + 2 : kb1 - 1);         // with WARM, always one touch last
+                warm(kb + 2 < kb1 ? kb + 2 : kb1 - 1);         // with WARM, always two touches last
             }
             const v8i af = af_next;
             if (i + 1 < TI) af_next = lds_frag(wt, wn * WTN + 16 * (i + 1) + r, g);
