@@ -153,6 +153,16 @@ def test_decode_strips_per_workgroup(strips, batch, M, N, monkeypatch):
     check_linear(x, w, f"decode strips={strips} batch={batch}")
 
 
+@pytest.mark.parametrize("M", [1, 3, 6, 8, 13])
+@pytest.mark.parametrize("K", [128, 256, 384, 640, 896])
+def test_decode_short_k(M, K):
+    """K shorter than a super block of the natural row group (the plan widens the group so
+    that one super block fits) and a last, partial super block whose weight scales are
+    loaded from K block KB - G."""
+    x, w = inputs(M, 384, K, seed=100 + M + K)
+    check_linear(x, w, f"decode short K={K}")
+
+
 @pytest.mark.parametrize("waves", [1, 2, 3, 5, 7, 8])
 def test_decode_split_counts(waves, monkeypatch):
     """Every split-K degree of the decode schedule meets the tolerance."""
