@@ -53,10 +53,11 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_HIP
 // Scratch of fp8_block_linear_noalloc: split-K partial sums (FP32 [split][M][N]),
 // written completely by the tile kernel before the reduce kernel reads them, so
 // nothing in it needs clearing between calls.  On a device of up to 256 CUs a split
-// keeps split x tiles <= 256 tiles of 128 x 128 partials, at most 16 MiB.  Each GPU
+// keeps split x tiles <= 256 tiles of 128 x 256 (or 128 x 128) partials, at most
+// 32 MiB (16 MiB with 128 x 128 tiles).  Each GPU
 // holds its own copy for the life of the process.  In host code `scratch` names a
 // host-side stand-in: kernels get the device address from hipGetSymbolAddress.
-constexpr size_t kNoAllocScratchBytes = size_t{16} << 20;
+constexpr size_t kNoAllocScratchBytes = size_t{32} << 20;
 static_assert(kNoAllocScratchBytes == FP8BS_NOALLOC_SCRATCH_BYTES, "header and library disagree");
 __device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
 std::atomic<void*> g_scratch[kMaxDevices];

@@ -430,9 +430,18 @@ static hipError_t launch_shape(PrefillArgs a, hipStream_t st) {
 // beat the weight-streaming mid-size kernel (measured on the 7168 x 7168
 // projection: 25.0 against 26.2 us at M = 48, 25.7 against 30.0 us at M = 64; at
 // M <= 32 the mid-size kernel is faster: 19.9 against 24.6 us at M = 32).
+// Tile columns of the split-K schedule: 256 from two tile rows of 128 on (M > 128,
+// N a multiple of 256), else 128.  Measured on the 7168 x 7168 projection, 128 x 256
+// split tiles against 128 x 128 (split or not): M = 160 / 256 / 300 / 384 / 512:
+// 42.5 / 43.6 / 67.2 / 67.4 / 67.9 -> 37.4 / 39.6 / 48.9 / 50.0 / 59.9 us (the wider
+// tiles halve the activation re-reads, and give a split where the 128 x 128 tiles
+// were too many to split); M = 128 the same, M = 48 - 96 slower (30.8 against 25.4 us
+// at M = 48).
+static int64_t prefill_split_bn(int64_t M, int64_t N) { return N % 256 == 0 && M > 128 ? 256 : 128; }
+
 int prefill_split(int64_t M, int64_t N, int64_t K, int cus) {
     if (M <= kSplitMinM) return 0;
-    const int64_t t = (M + 127) / 128 * (N / 128);
+    const int64_t t = (M + 127) / 128 * (N / prefill_split_bn(M, N));
     if (t >= cus - cus / 8) return 0;
     int64_t split = cus / t;
     if (split > kPrefillMaxSplit) split = kPrefillMaxSplit;
@@ -500,11 +509,11 @@ hipError_t launch_gemm_prefill(const void* q, const float* s, const void* w, con
         if (t == 256128 || t == 128128 || (n256 && (t == 256256 || t == 128256))) tile = t;
     }
     // Few tiles (a batch of up to a few hundred tokens): with a workspace, split K
-    // over the workgroups of each 128 x 128 tile; FP32 partial sums, then a reduce
-    // kernel adds them in a fixed order.
+    // over the workgroups of each 128 x 128 or 128 x 256 tile (prefill_split_bn);
+    // FP32 partial sums, then a reduce kernel adds them in a fixed order.
     const int split = prefill_plan_split(M, N, K, cus, workspace ? workspace_bytes : 0);
     if (split >= 2) {
-        tile = 128128;
+        tile = prefill_split_bn(M, N) == 256 ? 128256 : 128128;
         a.ksplit = split;
         a.part = (float*)workspace;
     }

@@ -161,7 +161,7 @@ int fp8_block_linear(const void* q_e4m3, const float* s_f32,
  * threads) race and must be serialized by the caller.  Nothing in the array needs
  * clearing: each call writes every partial it reads.
  */
-#define FP8BS_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+#define FP8BS_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 int fp8_block_linear_noalloc(const void* q_e4m3, const float* s_f32,
                              const void* w_e4m3, const float* ws_f32,
                              void* y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
@@ -218,7 +218,7 @@ const char* fp8bs_status_string(int status);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int fp8bs_abi_version(void);
 
-#define FP8BS_ABI_VERSION 10300
+#define FP8BS_ABI_VERSION 10400
 
 #ifdef __cplusplus
 }

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8bs_abi_version() == 10300
+    assert L.fp8bs_abi_version() == 10400
     for st in (OK, ENULL, ESHAPE, EALIGN, EDEV, EHIP, EWS, EVAL):
         assert L.fp8bs_status_string(st)
     assert b"unknown" in L.fp8bs_status_string(12345)
@@ -104,9 +104,11 @@ def test_block_linear_noalloc_validation(L):
     assert f(A16 + 4, A16b, A16c, A16d, A16e, 4, 128, 128, None) == EALIGN
     assert f(A16, A16b, A16c, A16d + 2, A16e, 4, 128, 128, None) == EALIGN
     assert f(None, None, None, None, None, 0, 128, 128, None) == OK     # M == 0
-    # The largest split-K workspace any valid shape asks for fits the static scratch.
-    for shape in ((33, 7168, 7168), (128, 7168, 7168), (100, 1024, 8192), (128, 16384, 7168), (200, 128, 8192)):
-        assert 0 < L.fp8_block_linear_workspace_size(*shape) <= 16 << 20, shape
+    # The largest split-K workspace any valid shape asks for fits the static scratch
+    # (32 MiB: at most 256 / t ways of t 128 x 256 tiles, so 256 * 256 * 4 * 128 bytes).
+    for shape in ((33, 7168, 7168), (128, 7168, 7168), (100, 1024, 8192), (128, 16384, 7168), (200, 128, 8192),
+                  (256, 7168, 7168), (384, 7168, 7168), (512, 7168, 7168), (256, 16384, 7168), (512, 1024, 8192)):
+        assert 0 < L.fp8_block_linear_workspace_size(*shape) <= 32 << 20, shape
 
 
 def test_nvfp4_linear_validation(L):

@@ -254,7 +254,10 @@ def test_subnormal_codes_and_scales():
 
 @pytest.mark.parametrize("M,N,K,split", [(65, 1024, 2048, None), (128, 2048, 7168, None), (200, 1024, 4096, None),
                                          (300, 1152, 2048, None), (128, 1024, 7168, "2"), (100, 512, 3072, "3"),
-                                         (129, 768, 4096, "8"), (80, 256, 512, "4")])
+                                         (129, 768, 4096, "8"), (80, 256, 512, "4"),
+                                         # 128 x 256 split tiles (M > 128, N a multiple of 256)
+                                         (300, 1024, 2048, None), (384, 2048, 4096, None), (129, 512, 3072, "5"),
+                                         (257, 768, 1152, "2"), (500, 1280, 2048, "3")])
 def test_split_k(M, N, K, split, monkeypatch):
     """Split-K over the workgroups of each tile (FP32 partials in the workspace, then a
     fixed-order reduce): within tolerance, and bitwise repeatable."""
