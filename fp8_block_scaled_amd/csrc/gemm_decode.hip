@@ -16,21 +16,23 @@
 //     columns, so decode shapes give many strips: the work per CU stays even (a CU
 //     that receives one strip more than another would set the kernel's time: a
 //     CU's own bandwidth is limited).
-//   * Split-K inside a workgroup: one workgroup per strip, its S waves take equal
+//   * Split-K inside a workgroup: one workgroup per NS strips, its S waves take equal
 //     contiguous ranges of "super blocks" (G K blocks each), and the partial sums
 //     over waves and groups are added through LDS in a fixed order
 //     (deterministic).  Partial sums never leave the workgroup: a reduction across
 //     workgroups would need agent-scope release / acquire, which on this part is
-//     a write-back / invalidate of the XCD's L2.
+//     a write-back / invalidate of the XCD's L2, or a second kernel (measured
+//     slower than the imbalance it removes).
 //   * Each workgroup owns NS adjacent strips; each wave loads one activation
 //     fragment per super block and uses it for the NS strips' MFMAs.  Every
 //     workgroup reads the whole M x K activation codes (from L2), so NS trades
 //     activation traffic against the number of workgroups; it is chosen per shape
 //     so that every CU receives as nearly the same number of strips as possible.
-//   * Each lane requests the fragments and scales of CH super blocks at a time.
-//     The weight scale index is made wave-uniform.  Weight loads read whole cache
-//     lines (a DPP exchange between partner lanes restores the operand layout) and
-//     are nontemporal.
+//   * Each lane requests the fragments and scales of CH super blocks (1 by
+//     default) before it uses any.  Weight loads read whole cache lines (a DPP
+//     exchange between partner lanes restores the operand layout) and are
+//     nontemporal; the weight scales of a super block come in one scalar load per
+//     strip.
 //
 // Operand layout per lane l (g = l / 16, r = l % 16, row rr = r % P, group
 // tb = r / P): A row r = weight row n0 + rr at K block kbase + tb; B column r =
@@ -39,7 +41,6 @@
 // is the same for A and B gives the same dot product).  The result lane l holds
 // C[4 g + e][r], e = 0..3: A row i = 4 g + e is weight row n0 + i % P of group
 // i / P, so the lane is on a diagonal block exactly when 4 g / P == tb.
-#include <climits>
 #include <cstdlib>
 
 #include "device_common.h"
