@@ -6,22 +6,22 @@
 //
 // Tiling: a workgroup of WM x WN waves (4 x 2 in the shapes launched) computes a
 // BM (m) x BN (n) output tile, each wave owning (BM/WM) x (BN/WN).  The K loop steps one
-// 128-wide scale block at a time through two LDS stages:
-//   1. at the top of step kb the wave waits for its own copies into stage kb%2
-//      and the workgroup meets at a barrier; the copies of K block kb + 1 into the
-//      other stage are then issued over the first subtile rows -- direct global ->
-//      LDS loads (global_load_lds_dwordx4: no VGPRs, no LDS write instructions),
-//      overlapping the compute of step kb.  A copy that the memory pipeline cannot
-//      take yet stalls its wave, MFMAs included, so with BN = 256 tiles waves 0-3
-//      (one per SIMD) issue all of them, 8 per subtile row over the first two rows
-//      (128 x 256: 4 per row over three rows), while the other wave on each SIMD
-//      keeps the MFMA pipe busy; 128 x 128 tiles spread them over every wave, two
-//      per row.  With 128 x 256 tiles the copying waves also touch every line of
-//      K block kb + 2 (4-byte direct-to-LDS loads into a dump area) so that the
-//      next copies find their lines in L2; measured, the touch pays for that shape
-//      (M = 768 on the 7168 x 7168 projection: 85 against 93 us, before the copying
-//      waves) and costs 2-8% on the others (its memory instructions outweigh the L2
-//      misses they save);
+// 128-wide scale block at a time through a ring of NST LDS stages (as many as the
+// 160 KiB of LDS holds: 2 for 256 x 256 tiles, 3 for 128 x 256 and 256 x 128, 4 for
+// 128 x 128), stage (kb - kb0) mod NST holding K block kb:
+//   1. during step kb the copies of K block kb + NST - 1 go into the stage that step
+//      kb - 1 read, issued over the first subtile rows -- direct global -> LDS loads
+//      (global_load_lds_dwordx4: no VGPRs, no LDS write instructions), overlapping the
+//      compute.  A copy that the memory pipeline cannot take yet stalls its wave,
+//      MFMAs included, so with BN = 256 tiles waves 0-3 (one per SIMD) issue all of
+//      them, 8 per subtile row over the first two rows (128 x 256: 4 per row over
+//      three rows), while the other wave on each SIMD keeps the MFMA pipe busy;
+//      128 x 128 tiles spread them over every wave, two per row.  At the end of the
+//      step each wave waits until its copies of K block kb + 1 have landed -- the
+//      NST - 2 younger stages' copies stay in flight -- and the workgroup meets at a
+//      barrier.  With two stages a step's copies must land within that step: with
+//      only 8 or 16 MFMAs per wave per step (128-row tiles) each step then lasted
+//      about one global-load latency;
 //   2. each wave runs v_mfma_f32_16x16x128_f8f6f4 over its 16 x 16 subtiles (A = 16
 //      weight rows, B = 16 token rows; one MFMA covers the whole K block) and folds
 //      each FP32 result into its accumulators with acc += (s[m] * ws[nb]) * P: the
@@ -68,8 +68,9 @@ struct PrefillArgs {
 // Bytes of one LDS stage: w tile, q tile, BM token scales, weight scales (one
 // wave's 4-byte copy writes 256 bytes; the first BN/128 are the tile's weight blocks).
 constexpr int stage_bytes(int BM, int BN) { return (BM + BN) * 128 + BM * 4 + 256; }
-// Tile shapes whose K loop touches the lines of K block kb + 2 ahead of the copies.
-constexpr bool prefill_warm(int BM, int BN) { return BM == 128 && BN == 256; }
+// LDS stages of the K loop's ring: as many as fit 160 KiB (stage_bytes: 66.8 KiB for
+// 256 x 256, 49-50 KiB for 128 x 256 and 256 x 128, 33.5 KiB for 128 x 128).
+constexpr int prefill_stages(int BM, int BN) { return BM == 256 && BN == 256 ? 2 : (BM == 128 && BN == 128 ? 4 : 3); }
 // Waves that issue the stage copies, and copies per subtile row.  256 x 256 tiles: 4
 // waves (one per SIMD), 8 per row -- measured against all 8 waves with 2 per row:
 // prefill_oproj 424 -> 412 us, fusion_fc 4.74 -> 4.52 ms, M = 2048 on the 7168 x 7168
@@ -79,8 +80,19 @@ constexpr bool prefill_warm(int BM, int BN) { return BM == 128 && BN == 256; }
 // that way (M = 64, split-K tiles: 25.7 -> 29.8 us), so they keep every wave, 2 per row.
 constexpr int prefill_copy_waves(int BM, int BN, int waves) { return BN == 256 ? 4 : waves; }
 constexpr int prefill_copies_per_row(int BM, int BN) { return BN == 256 ? (BM == 256 ? 8 : 4) : 2; }
-// Dynamic LDS of a launch: two stages, plus the 256-byte dump of the warm-up touches.
-constexpr int prefill_lds_bytes(int BM, int BN) { return 2 * stage_bytes(BM, BN) + (prefill_warm(BM, BN) ? 256 : 0); }
+// Dynamic LDS of a launch: the ring of stages.
+constexpr int prefill_lds_bytes(int BM, int BN) { return prefill_stages(BM, BN) * stage_bytes(BM, BN); }
+static_assert(prefill_lds_bytes(256, 256) <= 160 * 1024 && prefill_lds_bytes(128, 256) <= 160 * 1024 &&
+                  prefill_lds_bytes(256, 128) <= 160 * 1024 && prefill_lds_bytes(128, 128) <= 160 * 1024,
+              "the stage ring fits the LDS");
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), expcnt not waited (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt in 6:4, lgkmcnt in 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
@@ -104,6 +116,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
     constexpr int WTM = BM / WM, WTN = BN / WN;        // wave tile (m, n)
     constexpr int TJ = WTM / 16, TI = WTN / 16;         // subtiles (m, n)
     constexpr int kStage = stage_bytes(BM, BN);
+    constexpr int NST = prefill_stages(BM, BN);
     // A stage is (BM + BN) / 8 copy units of 8 tile rows (1 KiB, one 64-lane
     // 16-byte direct-to-LDS load); copying wave w takes kUnitsLo or kUnitsLo + 1 of
     // them.
@@ -183,11 +196,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
         const int R = 8 * u;
         uint32_t off = voff[u & 1];
         if (CLAMP && R >= BN) {
-            // rows past M read row M - 1 (never stored)
-            const int64_t row = (int64_t)((cbase[c] - a.x) / a.K);
-            int64_t lr = row + lrow;
-            lr = lr < a.M ? lr : a.M - 1;
-            off = (uint32_t)((lr - row) * a.K) + (voff[u & 1] - (uint32_t)(lrow * a.K));
+            // rows past M read row M - 1 (never stored); the unit's base row is
+            // min(r0, M - 1), so lane row min(r0 + lrow, M - 1) is 0..7 rows past it
+            const int64_t r0 = m0 + (R - BN);
+            const int64_t crow = r0 < a.M ? r0 : a.M - 1;
+            const int64_t lr = r0 + lrow < a.M ? r0 + lrow : a.M - 1;
+            off = (uint32_t)(lr - crow) * (uint32_t)a.K + (voff[u & 1] - (uint32_t)(lrow * a.K));
         }
         // The empty asm keeps the per-iteration scalar address opaque, so the lane
         // offset is added at the load (scalar base + 32-bit offset) instead of being
@@ -201,38 +215,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
     auto copy_stage = [&](int64_t kb, int stage) {
 #pragma unroll
         for (int c = 0; c < kCopies; ++c) copy_one(kb, stage, c);
-    };
-
-    // ---- L2 warm-up of K block kb + 2 (WARM shapes): the copying waves touch every
-    // stage row, thread t rows t and t + 64 kCopyWaves (mod BM + BN), one line each,
-    // always as the wave's last two vector loads; the other waves issue none (a vector
-    // memory instruction on them costs their MFMAs: M = 640 / 768 / 1024 on the
-    // 7168 x 7168 projection, 83.4 / 85.0 / 92.6 us with one touch per thread of every
-    // wave, 78.6 / 81.1 / 90.8 us this way).
-    constexpr bool WARM = prefill_warm(BM, BN);
-    static_assert(!WARM || BM + BN <= 2 * 64 * kCopyWaves, "two warm-up lines per copying thread cover the stage");
-    const int pf_row0 = tid % (BM + BN), pf_row1 = (tid + 64 * kCopyWaves) % (BM + BN);
-    const bool pf_w0 = pf_row0 < BN, pf_w1 = pf_row1 < BN;
-    int64_t pf_off0, pf_off1;
-    {
-        int64_t row = pf_w0 ? n0 + pf_row0 : m0 + (pf_row0 - BN);
-        if (CLAMP && !pf_w0) row = row < a.M ? row : a.M - 1;
-        pf_off0 = row * a.K;
-        row = pf_w1 ? n0 + pf_row1 : m0 + (pf_row1 - BN);
-        if (CLAMP && !pf_w1) row = row < a.M ? row : a.M - 1;
-        pf_off1 = row * a.K;
-    }
-    auto warm = [&](int64_t kb) {
-        if constexpr (WARM) {
-            if (wave < kCopyWaves) {                    // wave-uniform
-                const uint8_t* b0 = (pf_w0 ? a.w : a.x) + kb * kGroup;
-                const uint8_t* b1 = (pf_w1 ? a.w : a.x) + kb * kGroup;
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(b0 + pf_off0),
-                                                 (__attribute__((address_space(3))) void*)(lds + 2 * kStage), 4, 0, 0);
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(b1 + pf_off1),
-                                                 (__attribute__((address_space(3))) void*)(lds + 2 * kStage), 4, 0, 0);
-            }
-        }
     };
 
     // ---- scales: the BM token scales and the weight-block scales of K block kb are
@@ -273,10 +255,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
 #pragma unroll
         for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    copy_stage(kb0, 0);
-    copy_scales(kb0, 0);
-    copy_wscales(kb0, 0);
-    warm(kb0 + 1 < kb1 ? kb0 + 1 : kb1 - 1);
+    // Prologue: K blocks kb0 .. kb0 + NST - 2 into stages 0 .. NST - 2 (past kb1 - 1
+    // the last block is repeated, so every stage and step issues the same loads).
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st) {
+        const int64_t k = kb0 + st < kb1 ? kb0 + st : kb1 - 1;
+        copy_stage(k, st);
+        copy_scales(k, st);
+        copy_wscales(k, st);
+    }
+    // Loads this wave issues per stage (wave-uniform).
+    const int c_w = ucount + (xs_copy ? 1 : 0) + (ws_copy ? 1 : 0);
 
     // Fragments of one step, read from LDS stage `st`: the TJ B fragments (token rows),
     // their promotion factors s[m] * ws[nb], and the first A fragment (weight rows).
@@ -295,25 +284,38 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
         for (int j = 0; j < TJ; ++j) bf[j] = lds_frag(xt, wm * WTM + 16 * j + r, g);
         af_next = lds_frag(wt, wn * WTN + r, g);
     };
-    // This wave's copies into a stage (and the scale loads) have landed -- with the
-    // warm-up, all but the last two loads issued, the touches -- and it has consumed every
-    // LDS read of the other stage; the barrier makes everyone's copies visible.  A
-    // plain s_barrier: __syncthreads() would add a full vmcnt(0) wait (its fence).  The
-    // empty asm statements keep the compiler from moving LDS accesses across it.
+    // This wave's copies (and scale loads) into the next stage have landed and it has
+    // consumed every LDS read of the current one; the barrier makes everyone's copies
+    // visible.  Loads complete in issue order, so the wait leaves in flight exactly the
+    // NST - 2 younger stages' loads, c_w per stage: vmcnt((NST - 2) c_w), an immediate,
+    // hence one branch per value c_w takes (kCopies or 0 copies, plus 0 or 1 scale
+    // load; any other count waits for everything).  A plain s_barrier: __syncthreads()
+    // would add a full vmcnt(0) wait (its fence).  The empty asm statements keep the
+    // compiler from moving LDS accesses across the wait and the barrier.
     auto stage_ready = [&]() {
-        if constexpr (WARM)
-            asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        asm volatile("" ::: "memory");
+        if constexpr (NST == 2) {
+            wait_vm_lgkm0<0>();
+        } else {
+            if (c_w == kCopies + 1)
+                wait_vm_lgkm0<(NST - 2) * (kCopies + 1)>();
+            else if (c_w == kCopies)
+                wait_vm_lgkm0<(NST - 2) * kCopies>();
+            else if (c_w == 1)
+                wait_vm_lgkm0<NST - 2>();
+            else
+                wait_vm_lgkm0<0>();
+        }
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
     stage_ready();
     load_frags(0);
 
+    int stage = 0;
     for (int64_t kb = kb0; kb < kb1; ++kb) {
-        const int stage = (int)((kb - kb0) & 1);
-        const bool more = kb + 1 < kb1;
+        const int fill = stage == 0 ? NST - 1 : stage - 1;     // the stage step kb - 1 read
+        const int nxt = stage + 1 == NST ? 0 : stage + 1;
         const uint8_t* wt = lds + stage * kStage;
         // Subtile row i: TJ independent MFMAs (own result registers), each followed by
         // the promotion of row i - 1's result in the same column (one row later than it
@@ -332,20 +334,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
 #pragma unroll
                 for (int j = 0; j < TJ; ++j) sc[j] = xsv[j] * wsc;
             }
-            // The copies of K block kb + 1 are spread over the first rows, so the
+            // The copies of K block kb + NST - 1 are spread over the first rows, so the
             // workgroup's vector-memory requests do not queue up at the top of the
             // step in front of its LDS reads; past the last K block they repeat it
-            // into the idle stage (no branch in the loop).
-            const int64_t kn = more ? kb + 1 : kb;
+            // (no branch in the loop, and the same loads every step).
+            const int64_t kn = kb + NST - 1 < kb1 ? kb + NST - 1 : kb1 - 1;
             if (i < kCopyRows) {
 #pragma unroll
                 for (int c = 0; c < kPer; ++c)
-                    if (kPer * i + c < kCopies) copy_one(kn, stage ^ 1, kPer * i + c);
+                    if (kPer * i + c < kCopies) copy_one(kn, fill, kPer * i + c);
             }
             if (i == kCopyRows - 1) {
-                copy_scales(kn, stage ^ 1);
-                copy_wscales(kn, stage ^ 1);
-                warm(kb + 2 < kb1 ? kb + 2 : kb1 - 1);         // with WARM, always two touches last
+                copy_scales(kn, fill);
+                copy_wscales(kn, fill);
             }
             const v8i af = af_next;
             if (i + 1 < TI) af_next = lds_frag(wt, wn * WTN + 16 * (i + 1) + r, g);
@@ -367,17 +368,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
         float sc_last[TJ];
 #pragma unroll
         for (int j = 0; j < TJ; ++j) sc_last[j] = sc[j];
-        // Past the last K block the other stage holds a repeat of this one: reading it
-        // keeps the loop free of branches (a branch here would keep both fragment sets
-        // alive across it).
+        // Past the last K block the next stage holds a repeat of the last block: reading
+        // it keeps the loop free of branches (a branch here would keep both fragment
+        // sets alive across it).
         stage_ready();
-        load_frags(stage ^ 1);
+        load_frags(nxt);
 #pragma unroll
         for (int j = 0; j < TJ; ++j) promote(acc[TI - 1][j], sc_last[j], pend[j]);
+        stage = nxt;
     }
 
-    // No direct-to-LDS load (the last warm-up touch) may still be in flight when
-    // the workgroup's LDS is released.
+    // No direct-to-LDS load (the repeats of the last K block) may still be in flight
+    // when the workgroup's LDS is released.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: lane holds y[m][n .. n + 3] for each (i, j)

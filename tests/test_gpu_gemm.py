@@ -182,6 +182,16 @@ def test_prefill_tile_shapes(tile, M, monkeypatch):
     check_linear(x, w, f"prefill tile {tile}", workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
 
 
+@pytest.mark.parametrize("tile", ["256256", "256128", "128256", "128128"])
+@pytest.mark.parametrize("M,K", [(100, 128), (257, 256), (130, 384), (300, 640), (200, 896)])
+def test_prefill_stage_ring(tile, M, K, monkeypatch):
+    """The K loop's ring of LDS stages (2 to 4 per tile shape) with fewer K blocks than
+    stages (the prologue repeats the last block) and with counts that wrap the ring."""
+    monkeypatch.setenv("FP8BS_PREFILL_TILE", tile)
+    x, w = inputs(M, 512, K, seed=7 * M + K)
+    check_linear(x, w, f"prefill tile {tile} K={K}", workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+
+
 def test_prefill_default_mid_tile():
     """M = 1024 on the 7168-wide projection: the default schedule picks 128 x 256 tiles."""
     x, w = inputs(1024, 7168, 1024, seed=97)
