@@ -25,7 +25,9 @@
 //   2. each wave runs v_mfma_f32_16x16x128_f8f6f4 over its 16 x 16 subtiles (A = 16
 //      weight rows, B = 16 token rows; one MFMA covers the whole K block) and folds
 //      each FP32 result into its accumulators with acc += (s[m] * ws[nb]) * P: the
-//      promotion of partial sums per 128-wide K block.
+//      promotion of partial sums per 128-wide K block;
+//   3. the epilogue rounds the tile to BF16 (or keeps FP32 split-K partial sums),
+//      passes it through the then-free stage ring and stores whole lines.
 // LDS rows are 128 bytes; 16-byte chunk c of tile row r is stored at chunk
 // position c ^ ((r >> 1) & 7), so the 16 rows a fragment read touches fall in 16
 // distinct 4-bank groups.  A direct-to-LDS load writes lane l's 16 bytes at
@@ -40,6 +42,7 @@
 // a grouped (2 tile-rows) raster order: tiles that share q rows or w rows then
 // share an XCD's L2.
 #include <cstdlib>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -93,6 +96,9 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
     static_assert(N >= 0 && N <= 63, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
@@ -382,24 +388,81 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_prefill_kernel(PrefillAr
     // when the workgroup's LDS is released.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // ---- epilogue: lane holds y[m][n .. n + 3] for each (i, j)
+    // ---- epilogue: lane holds y[m][n .. n + 3] for each (i, j), as FP32 partial sums
+    // (split-K) or rounded to BF16.  Stored straight from the accumulator layout, each
+    // store instruction writes 32- (BF16) or 64-byte (FP32) pieces of 16 rows, and a
+    // 256 x 256 BF16 tile took about 9.5 us to write (4.7 us to issue wave 0's stores,
+    // 5 us to drain them) against a 110 us K loop.  Instead each wave puts its
+    // WTM x WTN tile into its own LDS region (the stages are free once every wave has
+    // finished its last fragment reads: the barrier), reads it back by rows and stores
+    // 16 bytes per lane, whole lines.  Region rows are WTN * EB bytes; 16-byte chunk c
+    // of region row m sits at chunk c ^ (m mod CPR), so that the rows an accumulator
+    // write covers fall in different banks.  FP32 tiles of 256 rows do not fit the
+    // ring; split-K never runs them, and they keep the direct stores.
+    const bool fp32_out = a.part != nullptr;
+    constexpr bool kStagedF32 = BM * BN * 4 <= prefill_lds_bytes(BM, BN);
+    static_assert(BM * BN * 2 <= prefill_lds_bytes(BM, BN), "the BF16 tile fits the stage ring");
+    if (!kStagedF32 && fp32_out) {
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-        if (!mok[j]) continue;
-        const int64_t m = m0 + wm * WTM + 16 * j + r;
+        for (int j = 0; j < TJ; ++j) {
+            if (!mok[j]) continue;
+            const int64_t m = m0 + wm * WTM + 16 * j + r;
 #pragma unroll
-        for (int i = 0; i < TI; ++i) {
-            const int64_t n = n0 + wn * WTN + 16 * i + 4 * g;
-            if (a.part) {                                      // split-K partial sums
+            for (int i = 0; i < TI; ++i) {
+                const int64_t n = n0 + wn * WTN + 16 * i + 4 * g;
                 *reinterpret_cast<v4f*>(a.part + ((int64_t)ks * a.M + m) * a.N + n) = acc[i][j];
-                continue;
             }
-            uint2 o;
-            o.x = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
-            o.y = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
-            *reinterpret_cast<uint2*>(a.y + m * a.N + n) = o;
         }
+        return;
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    auto staged = [&](auto eb) {
+        constexpr int EB = decltype(eb)::value;                // bytes per element: 2 or 4
+        constexpr int RB = WTN * EB;                           // region row bytes
+        constexpr int CPR = RB / 16;                           // 16-byte chunks per region row
+        constexpr int RPI = 64 / CPR;                          // region rows per read instruction
+        static_assert(RB % 16 == 0 && 64 % CPR == 0 && WTM % RPI == 0, "epilogue row mapping");
+        uint8_t* region = lds + wave * (WTM * RB);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+            const int ml = 16 * j + r;
+#pragma unroll
+            for (int i = 0; i < TI; ++i) {
+                // n = 16 i + 4 g .. + 3 within the wave tile
+                if constexpr (EB == 4) {
+                    *reinterpret_cast<v4f*>(region + ml * RB + (((4 * i + g) ^ (ml % CPR)) << 4)) = acc[i][j];
+                } else {
+                    const bf16x2 lo = __builtin_convertvector(f32x2{acc[i][j][0], acc[i][j][1]}, bf16x2);
+                    const bf16x2 hi = __builtin_convertvector(f32x2{acc[i][j][2], acc[i][j][3]}, bf16x2);
+                    uint2 o;
+                    __builtin_memcpy(&o.x, &lo, 4);
+                    __builtin_memcpy(&o.y, &hi, 4);
+                    const int chunk = 2 * i + (g >> 1);
+                    *reinterpret_cast<uint2*>(region + ml * RB + ((chunk ^ (ml % CPR)) << 4) + (g & 1) * 8) = o;
+                }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int rl = lane / CPR, cl = lane % CPR;
+#pragma unroll
+        for (int it = 0; it < WTM / RPI; ++it) {
+            const int ml = it * RPI + rl;
+            const v4i v = *reinterpret_cast<const v4i*>(region + ml * RB + ((cl ^ (ml % CPR)) << 4));
+            const int64_t m = m0 + wm * WTM + ml;
+            if (CLAMP && m >= a.M) continue;
+            const int64_t n = n0 + wn * WTN + (16 / EB) * cl;
+            if constexpr (EB == 4)
+                *reinterpret_cast<v4i*>(a.part + ((int64_t)ks * a.M + m) * a.N + n) = v;
+            else
+                *reinterpret_cast<v4i*>(a.y + m * a.N + n) = v;
+        }
+    };
+    if (kStagedF32 && fp32_out)
+        staged(std::integral_constant<int, 4>{});
+    else
+        staged(std::integral_constant<int, 2>{});
 }
 
 template <int BM, int BN, int WM, int WN, bool CLAMP>
