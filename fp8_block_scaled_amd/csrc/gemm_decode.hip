@@ -16,10 +16,11 @@
 //     columns, so decode shapes give many strips: the work per CU stays even (a CU
 //     that receives one strip more than another would set the kernel's time: a
 //     CU's own bandwidth is limited).
-//   * Split-K inside a workgroup: one workgroup per NS strips, its S waves take equal
-//     contiguous ranges of "super blocks" (G K blocks each), and the partial sums
-//     over waves and groups are added through LDS in a fixed order
-//     (deterministic).  Partial sums never leave the workgroup: a reduction across
+//   * Split-K inside a workgroup: one workgroup per NS strips, its S waves split the
+//     "super blocks" (G K blocks each) evenly -- as contiguous ranges, or interleaved
+//     (wave w takes w, w + S, ...: at any moment the workgroup reads one stretch of
+//     each weight row), chosen per shape -- and the partial sums over waves and
+//     groups are added through LDS in a fixed order (deterministic).  Partial sums never leave the workgroup: a reduction across
 //     workgroups would need agent-scope release / acquire, which on this part is
 //     a write-back / invalidate of the XCD's L2, or a second kernel (measured
 //     slower than the imbalance it removes).
@@ -54,7 +55,10 @@ typedef float f32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 // At most 8 waves per workgroup: the launch bound then allows 128+ VGPRs per wave,
 // so 4 strips with two super blocks per batch (136 VGPRs) do not spill.  A bound of
 // 16 waves capped them at 128 and spilled; the 8-wave bound measured 2.5% faster at
-// M = 8, N = 16384, K = 7168 and equal elsewhere.
+// M = 8, N = 16384, K = 7168 and equal elsewhere.  A 16-wave bound for the one-batch
+// kernels alone (which fit 128 registers) was slower at 8 waves (M = 8, N = 7168,
+// K = 8192: 13.68 against 13.19-13.26 us) and at 12 or 16 waves on every decode
+// workload.
 constexpr int kDecodeMaxWaves = 8;
 // Workgroup shape, from measurement on the decode shapes (M = 1 and 8, K = 7168
 // and 8192, N = 7168..16384): 8 waves per workgroup; fewer leave a CU short of
@@ -72,6 +76,7 @@ struct DecodeArgs {
     int M;
     int64_t N, K, KB;
     int64_t strips;                          // N / P
+    int interleave;                          // 1: wave w takes super blocks w, w + S, ...; 0: a contiguous range
 };
 
 template <int P, int NS, int CH>
@@ -86,8 +91,9 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
     const bool mvalid = rr < a.M;
     const int64_t strip0 = (int64_t)blockIdx.x * NS;
     const int64_t SKB = (a.KB + G - 1) / G;
-    const int64_t sb0 = (wave * SKB) / S;
-    const int64_t sb1 = ((wave + 1) * SKB) / S;
+    const int64_t sb0 = a.interleave ? wave : (wave * SKB) / S;
+    const int64_t sb1 = a.interleave ? SKB : ((wave + 1) * SKB) / S;
+    const int64_t sstep = a.interleave ? S : 1;
     const uint8_t* xrow = a.x + (mvalid ? rr : 0) * a.K + 16 * g;
     const float* xsrow = a.xs + (mvalid ? rr : 0) * a.KB;
     // Weight loads read whole 128-byte lines.  Lanes r and r ^ 8 of a 16-lane row
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
 
     // A batch: fragments and scales of CH super blocks, all requested before any is
     // used.  Branch-free, so that no load is sunk past another super block's MFMAs:
-    // a super block past the wave's range re-reads the wave's last one, a K block
+    // a super block past the wave's range re-reads super block sb1 - 1, a K block
     // past KB (a last, partial super block) is clamped to the last K block, and both
     // are zeroed at use.
     v4i wv[CH][NS][2], xv[CH][2];
@@ -138,7 +144,7 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
     auto load_batch = [&](int64_t sb) {
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            const int64_t sbi = sb + i < sb1 ? sb + i : sb1 - 1;
+            const int64_t sbi = sb + i * sstep < sb1 ? sb + i * sstep : sb1 - 1;
             int64_t k = sbi * G + tb, kA = sbi * G + tbA, kB = sbi * G + tbB;
             k = k < a.KB ? k : a.KB - 1;
             kA = kA < a.KB ? kA : a.KB - 1;
@@ -175,12 +181,12 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
     for (int q = 0; q < NS; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
     const v4i z4 = {0, 0, 0, 0};
-    for (int64_t sb = sb0; sb < sb1; sb += CH) {
+    for (int64_t sb = sb0; sb < sb1; sb += CH * sstep) {
         load_batch(sb);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            const bool use = mvalid && sb + i < sb1 && (sb + i) * G + tb < a.KB;
+            const bool use = mvalid && sb + i * sstep < sb1 && (sb + i * sstep) * G + tb < a.KB;
             const v4i b0 = use ? xv[i][0] : z4, b1 = use ? xv[i][1] : z4;
             const v8i bv = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
             const float xsc = use ? xsv[i] : 0.0f;
@@ -269,6 +275,15 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int cus) {
         const int v = atoi(e);
         if (v >= 1 && v <= 2) p.batch = v;
     }
+    // Interleaved super blocks, except where a weight row is a multiple of 8 KiB.
+    // Same-session rounds on three boxes (graph-timed, 8 waves): q/k/v (K = 7168)
+    // 12.07-12.17 / 12.09-12.13 / 12.28-12.29 against 12.21-12.22 / 12.25-12.30 /
+    // 12.43-12.51 us contiguous; gate/up (K = 7168) 20.42-20.49 / 20.57 / 20.88-20.94
+    // against 20.9-21.2 / 20.94-21.27 / 21.28-21.48; down (K = 8192) 15.2 / 15.0-15.1 /
+    // 14.7-14.8 against 13.3 / 13.2-13.3 / 13.4 (slower at every wave count tried,
+    // 3-8; visiting each workgroup's super blocks in a rotated order was slower still).
+    p.interleave = (K % 8192) != 0;
+    if (const char* e = getenv("FP8BS_DECODE_INTERLEAVE")) p.interleave = atoi(e) != 0;   // tuning hook
     return p;
 }
 
@@ -300,6 +315,7 @@ hipError_t launch_gemm_decode(const DecodePlan& plan, const void* q, const float
     a.K = K;
     a.KB = plan.kblocks;
     a.strips = plan.strips;
+    a.interleave = plan.interleave;
     const dim3 grid((unsigned)plan.workgroups), block(plan.waves * 64);
     const unsigned lds = (unsigned)(plan.waves * plan.strips_per_wg * 64 * sizeof(v4f));
     switch (plan.rows) {

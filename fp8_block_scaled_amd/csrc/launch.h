@@ -63,6 +63,7 @@ struct DecodePlan {
     int64_t kblocks;     // K / 128
     int waves;           // waves per workgroup = K splits
     int batch;           // super blocks whose loads are issued together (1 or 2)
+    int interleave;      // 1: wave w of S takes super blocks w, w + S, ...; 0: contiguous ranges
 };
 
 DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int cus);

@@ -140,15 +140,18 @@ def test_decode_activations_beyond_lds(M, K):
     check_linear(x, w, "decode, activations from global")
 
 
+@pytest.mark.parametrize("interleave", [0, 1])
 @pytest.mark.parametrize("batch", [1, 2])
 @pytest.mark.parametrize("strips", [1, 2, 3, 4])
 @pytest.mark.parametrize("M,N", [(1, 640), (5, 384), (8, 1152), (12, 640)])
-def test_decode_strips_per_workgroup(strips, batch, M, N, monkeypatch):
+def test_decode_strips_per_workgroup(strips, batch, interleave, M, N, monkeypatch):
     """Every strips-per-workgroup setting and load batch (super blocks whose loads
-    are issued together), including a partial last workgroup, a partial last
-    super block (K = 1408: 11 K blocks) and a partial last batch."""
+    are issued together), with contiguous and interleaved super blocks per wave,
+    including a partial last workgroup, a partial last super block (K = 1408: 11 K
+    blocks) and a partial last batch."""
     monkeypatch.setenv("FP8BS_DECODE_STRIPS", str(strips))
     monkeypatch.setenv("FP8BS_DECODE_BATCH", str(batch))
+    monkeypatch.setenv("FP8BS_DECODE_INTERLEAVE", str(interleave))
     x, w = inputs(M, N, 1408, seed=80 + strips + M)
     check_linear(x, w, f"decode strips={strips} batch={batch}")
 
@@ -163,10 +166,13 @@ def test_decode_short_k(M, K):
     check_linear(x, w, f"decode short K={K}")
 
 
+@pytest.mark.parametrize("interleave", [0, 1])
 @pytest.mark.parametrize("waves", [1, 2, 3, 5, 7, 8])
-def test_decode_split_counts(waves, monkeypatch):
-    """Every split-K degree of the decode schedule meets the tolerance."""
+def test_decode_split_counts(waves, interleave, monkeypatch):
+    """Every split-K degree of the decode schedule meets the tolerance, with
+    contiguous and interleaved super blocks per wave."""
     monkeypatch.setenv("FP8BS_DECODE_WAVES", str(waves))
+    monkeypatch.setenv("FP8BS_DECODE_INTERLEAVE", str(interleave))
     x, w = inputs(5, 384, 2048, seed=50 + waves)
     check_linear(x, w, f"decode waves={waves}")
 
