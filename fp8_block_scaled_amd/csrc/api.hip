@@ -160,7 +160,7 @@ int linear_check(const void* q_e4m3, const float* s_f32, const void* w_e4m3, con
 int linear_dispatch(const void* q_e4m3, const float* s_f32, const void* w_e4m3, const float* ws_f32, void* y_bf16,
                     int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, int cus,
                     hipStream_t stream) {
-    if (M <= fp8bs::kDecodeMaxM) {
+    if (M <= fp8bs::kDecodeMaxM && K <= fp8bs::decode_max_k()) {
         const fp8bs::DecodePlan plan = fp8bs::plan_decode(M, N, K, cus);
         return hip_status(
             fp8bs::launch_gemm_decode(plan, q_e4m3, s_f32, w_e4m3, ws_f32, y_bf16, M, N, K, stream));

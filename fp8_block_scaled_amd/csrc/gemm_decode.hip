@@ -115,16 +115,21 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
     const int pA = r ^ (8 * hh), pB = pA ^ 8;
     const int rowA = pA % P, tbA = pA / P, rowB = pB % P, tbB = pB / P;
     const int cw = 16 * (g + 4 * hh);
-    const uint8_t* wrowA[NS];
-    const uint8_t* wrowB[NS];
+    // Strip bases are wave-uniform (scalar registers); the lane's offset within a strip
+    // is 32-bit and the same for every strip (below (P + 1) K, so K <= kDecodeMaxK keeps
+    // it in range).  Against 64-bit lane addresses per strip: 67 instead of 72 registers
+    // with 3 strips, 79 instead of 88 with 4; same-box A/B, two rounds: M = 8, N = 7168,
+    // K = 8192 13.28-13.34 against 13.50-13.58 us, M = 8, N = 16384 20.38-20.66 against
+    // 20.46-21.76, M = 1, N = 9216 12.11-12.42 against 12.16-12.56.
+    const uint8_t* wst[NS];
+    const uint32_t offA = (uint32_t)(rowA * a.K + cw), offB = (uint32_t)(rowB * a.K + cw);
     const float* wsrow[NS];
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
         // Strips past the last one (a partial final workgroup) re-read the last
         // strip; their results are not stored.
         const int64_t st = strip0 + q < a.strips ? strip0 + q : a.strips - 1;
-        wrowA[q] = a.w + (st * P + rowA) * a.K + cw;
-        wrowB[q] = a.w + (st * P + rowB) * a.K + cw;
+        wst[q] = a.w + st * P * a.K;
         wsrow[q] = a.ws + ((st * P) / kGroup) * a.KB;
     }
 
@@ -157,8 +162,10 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
             xsv[i] = xsrow[k];
 #pragma unroll
             for (int q = 0; q < NS; ++q) {
-                wv[i][q][0] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrowA[q] + kA * kGroup));
-                wv[i][q][1] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrowB[q] + kB * kGroup));
+                wv[i][q][0] = __builtin_nontemporal_load(
+                    reinterpret_cast<const v4i*>(wst[q] + (offA + (uint32_t)kA * (uint32_t)kGroup)));
+                wv[i][q][1] = __builtin_nontemporal_load(
+                    reinterpret_cast<const v4i*>(wst[q] + (offB + (uint32_t)kB * (uint32_t)kGroup)));
                 if constexpr (G == 4) {
                     const f32x4_a4 v = *reinterpret_cast<const f32x4_a4*>(wsrow[q] + wbase);
                     wsg[i][q][0] = v[0];
@@ -240,6 +247,14 @@ __global__ __launch_bounds__(kDecodeMaxWaves * 64) void gemm_decode_kernel(Decod
             a.y[m * a.N + (strip0 + q) * P + c] = (uint16_t)f32_to_bf16_rne(sum);
         }
     }
+}
+
+int64_t decode_max_k() {
+    if (const char* e = getenv("FP8BS_DECODE_MAX_K")) {     // test hook: route longer rows to the mid-size kernel
+        const long long v = atoll(e);
+        if (v > 0 && v < kDecodeMaxK) return v;
+    }
+    return kDecodeMaxK;
 }
 
 // Row-group size for M tokens: the smallest of 4, 8, 16 that holds them.

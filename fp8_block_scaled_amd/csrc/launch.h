@@ -33,6 +33,11 @@ hipError_t launch_quant_weight(const void* w, void* qw, float* ws, int64_t N, in
 
 // ---- decode GEMM (M <= kDecodeMaxM): one workgroup per strip of `rows` columns, split-K over its waves
 constexpr int kDecodeMaxM = 16;
+// ... and K <= kDecodeMaxK: its per-lane weight offsets are 32-bit (below 17 K).  Longer
+// rows take the mid-size kernel (64-bit addresses; rows past M repeat row M - 1).
+constexpr int64_t kDecodeMaxK = int64_t{1} << 27;
+// kDecodeMaxK, or a lower bound set by the FP8BS_DECODE_MAX_K test hook.
+int64_t decode_max_k();
 
 // Strips per workgroup for the weight-streaming decode kernels.  Workgroups go
 // round-robin to the CUs and a CU's own bandwidth is limited, so the time follows

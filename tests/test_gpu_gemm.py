@@ -156,6 +156,16 @@ def test_decode_strips_per_workgroup(strips, batch, interleave, M, N, monkeypatc
     check_linear(x, w, f"decode strips={strips} batch={batch}")
 
 
+@pytest.mark.parametrize("M,K", [(1, 1152), (5, 2048), (16, 1408), (3, 1024)])
+def test_decode_rows_past_the_decode_bound(M, K, monkeypatch):
+    """Rows longer than the decode kernel's bound (2^27, lowered to 1024 by the test
+    hook) take the mid-size kernel, also for M <= 16; K = 1024 stays on the decode
+    kernel."""
+    monkeypatch.setenv("FP8BS_DECODE_MAX_K", "1024")
+    x, w = inputs(M, 384, K, seed=660 + M + K)
+    check_linear(x, w, f"decode bound K={K}")
+
+
 @pytest.mark.parametrize("M", [1, 3, 6, 8, 13])
 @pytest.mark.parametrize("K", [128, 256, 384, 640, 896])
 def test_decode_short_k(M, K):
