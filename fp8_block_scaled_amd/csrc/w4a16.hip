@@ -243,16 +243,19 @@ __global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_decode_kernel(W4Args a
     const int64_t sb0 = (wave * SB) / S;
     const int64_t sb1 = ((wave + 1) * SB) / S;
     const uint16_t* xrow = a.x + (int64_t)(mvalid ? j : 0) * a.K + 32 * g;
-    const uint8_t* wrow[NS];
-    const uint8_t* srow[NS];
+    // Strip bases are wave-uniform (scalar registers); the lane's offsets within a strip
+    // are 32-bit and the same for every strip (below (P + 1) K / 2, so K <= kDecodeMaxK
+    // keeps them in range).
+    const uint8_t* wst[NS];
+    const uint8_t* sst[NS];
+    const uint32_t woff = (uint32_t)(j * (a.K / 2) + 16 * g), soff = (uint32_t)(j * (a.K / 16) + 2 * g);
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
         // Strips past the last one (a partial final workgroup) re-read the last
         // strip; their results are not stored.
         const int64_t st = strip0 + q < a.strips ? strip0 + q : a.strips - 1;
-        const int64_t n = st * P + j;
-        wrow[q] = a.w + n * (a.K / 2) + 16 * g;
-        srow[q] = a.bs + n * (a.K / 16) + 2 * g;
+        wst[q] = a.w + st * P * (a.K / 2);
+        sst[q] = a.bs + st * P * (a.K / 16);
     }
 
     v4i wv[CH][NS], xv[CH][4];
@@ -270,8 +273,9 @@ __global__ __launch_bounds__(kW4MaxWaves * 64) void w4a16_decode_kernel(W4Args a
             for (int q = 0; q < NS; ++q) {
                 // Nontemporal: the code stream is read once; at P = 4 and 8 one load
                 // instruction covers whole 128-byte lines (G adjacent K blocks of a row).
-                wv[i][q] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow[q] + kc * 64));
-                sv[i][q] = *reinterpret_cast<const uint16_t*>(srow[q] + kc * 8);
+                wv[i][q] = __builtin_nontemporal_load(
+                    reinterpret_cast<const v4i*>(wst[q] + (woff + (uint32_t)kc * 64u)));
+                sv[i][q] = *reinterpret_cast<const uint16_t*>(sst[q] + (soff + (uint32_t)kc * 8u));
             }
         }
     };
@@ -628,7 +632,7 @@ W4Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cus, size_t workspace_byt
     }
     // Decode: K chunks folded into the MFMA; NS strips of P columns per workgroup.
     const char* de = getenv("FP8BS_W4_DECODE");              // tuning hook: 0 = stream kernel
-    if (M <= 16 && !(de && atoi(de) == 0)) {
+    if (M <= 16 && K <= decode_max_k() && !(de && atoi(de) == 0)) {
         const int P = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
         p.decode_p = P;
         const int64_t strips = N / P;

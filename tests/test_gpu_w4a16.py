@@ -128,6 +128,9 @@ DECODE_CASES = [
     (9, 8576, 1024, {"FP8BS_W4_DECODE_NS": "4", "FP8BS_W4_DECODE_CH": "2"}),
     (16, 2048, 384, {"FP8BS_W4_DECODE_NS": "2", "FP8BS_W4_DECODE_CH": "2"}),
     (5, 1152, 384, {"FP8BS_W4_DECODE_NS": "2", "FP8BS_W4_DECODE_CH": "1"}),
+    # rows past the decode kernel's bound (lowered from 2^27 by the test hook) stream
+    (1, 2048, 384, {"FP8BS_DECODE_MAX_K": "1024"}),
+    (7, 1152, 640, {"FP8BS_DECODE_MAX_K": "1024"}),
 ]
 
 
